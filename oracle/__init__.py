@@ -1,0 +1,163 @@
+"""fp64 CPU oracle for tiled exact attention -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP library
+(``tiled_exact_attention_amd``) and never imports it.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, OpenMP over
+output rows); this module only builds that file with gcc and marshals numpy
+arrays through ctypes.  See ``oracle.c`` for the definition it follows and the
+readings of the source pages it adopts.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_libs: dict = {}
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile a C source of the oracle into a shared library with gcc."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (no fast-math, no intrinsics)."""
+    if force or not os.path.exists(_LIB):
+        compile_source(SOURCE, _LIB)
+    return _LIB
+
+
+def _load(path: str | None = None):
+    if path is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        path = _LIB
+    if path not in _libs:
+        lib = ctypes.CDLL(path)
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        vp = ctypes.c_void_p
+        lib.oracle_fwd_rows.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        f64, i32, i32, vp, i64, vp, vp, i32]
+        lib.oracle_fwd_rows.restype = i32
+        lib.oracle_decode_int8_rows.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                f64, vp, i64, vp, vp, i32]
+        lib.oracle_decode_int8_rows.restype = i32
+        lib.oracle_max_threads.argtypes = [i32]
+        lib.oracle_max_threads.restype = i32
+        _libs[path] = lib
+    return _libs[path]
+
+
+def _f64(x) -> np.ndarray:
+    """Widen to a contiguous float64 array (exact for bf16/fp16/fp32 values)."""
+    if hasattr(x, "detach"):  # a torch tensor: widen on its own side, then hand over
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _np(x, dtype) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    a = np.asarray(x)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads(threads: int = 0) -> int:
+    """Threads the oracle's OpenMP regions use (threads=0: OpenMP default)."""
+    return int(_load().oracle_max_threads(int(threads)))
+
+
+def fwd(q, k, v, *, causal: bool, window: int = 0, scale: float | None = None,
+        rows=None, threads: int = 0, lib: str | None = None):
+    """Exact attention in fp64.
+
+    q: [B, Sq, Hq, d]; k, v: [B, Skv, Hkv, d] (any real dtype, widened to fp64).
+    rows: None for every output row, else an int array of shape [n, 3] holding
+    (b, h, i) triples.  Returns (o, lse): with rows=None o is [B, Sq, Hq, d] and
+    lse [B, Hq, Sq]; otherwise o is [n, d] and lse [n].  lse is the natural log
+    of the sum over visible keys of exp(scale * q.k).
+    lib: path of an alternative build of the oracle source (tests only).
+    """
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    B, Sq, Hq, d = qd.shape
+    Bk, Skv, Hkv, dk = kd.shape
+    if (Bk, dk) != (B, d) or vd.shape != kd.shape:
+        raise ValueError("shape mismatch between q, k and v")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    full = rows is None
+    if full:
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(Sq), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load(lib).oracle_fwd_rows(_ptr(qd), _ptr(kd), _ptr(vd), B, Hq, Hkv, Sq, Skv, d,
+                                 float(scale), int(bool(causal)), int(window),
+                                 _ptr(rows), n, _ptr(o), _ptr(lse), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_fwd_rows rejected its arguments (code {rc})")
+    if full:
+        o = o.reshape(B, Hq, Sq, d).transpose(0, 2, 1, 3).copy()
+        lse = lse.reshape(B, Hq, Sq)
+    return o, lse
+
+
+def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
+                rows=None, threads: int = 0, lib: str | None = None):
+    """Decode attention of one query token over an int8 KV cache, in fp64.
+
+    q: [B, Hq, d] (widened to fp64); kq, vq: [B, Hkv, Skv, d] int8;
+    k_scale, v_scale: [B, Hkv, Skv] float32.  Every cached key is visible.
+    rows: None for all (b, h), else an int array [n, 2] of (b, h) pairs.
+    Returns (o, lse) shaped [B, Hq, d] and [B, Hq], or [n, d] and [n].
+    lib: path of an alternative build of the oracle source (tests only).
+    """
+    qd = _f64(q)
+    kqa, vqa = _np(kq, np.int8), _np(vq, np.int8)
+    ksa, vsa = _np(k_scale, np.float32), _np(v_scale, np.float32)
+    B, Hq, d = qd.shape
+    Bk, Hkv, Skv, dk = kqa.shape
+    if (Bk, dk) != (B, d) or vqa.shape != kqa.shape:
+        raise ValueError("shape mismatch between q and the cache")
+    if ksa.shape != (B, Hkv, Skv) or vsa.shape != (B, Hkv, Skv):
+        raise ValueError("scale arrays must be [B, Hkv, Skv]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    full = rows is None
+    if full:
+        bb, hh = np.meshgrid(np.arange(B), np.arange(Hq), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel()], axis=1)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load(lib).oracle_decode_int8_rows(_ptr(qd), _ptr(kqa), _ptr(ksa), _ptr(vqa), _ptr(vsa),
+                                         B, Hq, Hkv, Skv, d, float(scale),
+                                         _ptr(rows), n, _ptr(o), _ptr(lse), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_decode_int8_rows rejected its arguments (code {rc})")
+    if full:
+        o = o.reshape(B, Hq, d)
+        lse = lse.reshape(B, Hq)
+    return o, lse

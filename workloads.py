@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for tiled exact attention (shared by tests, smoke and bench).
+
+This module only draws random tensors and names the workloads; it holds none
+of the attention arithmetic, imports neither the HIP library nor the oracle,
+and is the one piece of code both sides of every parity check share.
+
+Workloads are shaped like the pages' examples: Llama-2-7B style MHA (32/32
+heads, d=128), Mistral-7B style GQA (32 query / 8 kv heads), Falcon-180B
+style MQA (232 / 1, d=64), S=4096 with batch 2, a 512-token sliding window and
+a 32K-token int8 KV cache.  Values are i.i.d. N(0, 1) from ``torch.randn`` on a
+seeded generator, drawn in the order Q, K, V and cast to bf16 by
+round-to-nearest-even where the workload is bf16.
+
+The int8 cache recipe (a reading: the pages name an int8 cache with no
+scheme): symmetric per (token, kv head), scale = absmax / 127 in fp32,
+code = clamp(round_half_even(x / scale), -127, 127); an all-zero row gets
+scale 0 and codes 0.  The consumers only ever see the stored codes and
+scales, so this rounding cannot influence parity.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Prefill:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    d: int
+    causal: bool
+    window: int
+    dtype: str  # "f32" or "bf16"
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+@dataclasses.dataclass(frozen=True)
+class Decode:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Skv: int
+    d: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The five workloads (plus the windowed variant of the MQA one).
+TINY_F32 = Prefill("tiny fp32 exact attention B1 H2 S128 d64 non-causal", 1, 2, 2, 128, 128, 64, False, 0, "f32", 0)
+MHA_CAUSAL = Prefill("MHA causal prefill bf16 B2 H32 S4096 d128", 2, 32, 32, 4096, 4096, 128, True, 0, "bf16", 1)
+GQA_CAUSAL = Prefill("GQA causal prefill bf16 B1 Hq32 Hkv8 S4096 d128", 1, 32, 8, 4096, 4096, 128, True, 0, "bf16", 2)
+MQA_CAUSAL = Prefill("MQA causal prefill bf16 B1 Hq232 Hkv1 S2048 d64", 1, 232, 1, 2048, 2048, 64, True, 0, "bf16", 3)
+MQA_WINDOW = Prefill("MQA causal sliding-window-512 prefill bf16 B1 Hq232 Hkv1 S2048 d64", 1, 232, 1, 2048, 2048, 64, True, 512, "bf16", 3)
+INT8_DECODE = Decode("GQA decode over int8 KV cache B32 Hq32 Hkv8 Skv32768 d128", 32, 32, 8, 32768, 128, 4)
+
+PREFILL_WORKLOADS = (TINY_F32, MHA_CAUSAL, GQA_CAUSAL, MQA_CAUSAL, MQA_WINDOW)
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _cast(x: torch.Tensor, dtype: str) -> torch.Tensor:
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    raise ValueError(dtype)
+
+
+def prefill_inputs(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", seed=0, device="cpu"):
+    """q [B,Sq,Hq,d], k/v [B,Skv,Hkv,d], i.i.d. N(0,1), drawn Q then K then V."""
+    g = _gen(seed, device)
+    q = torch.randn((B, Sq, Hq, d), generator=g, device=device, dtype=torch.float32)
+    k = torch.randn((B, Skv, Hkv, d), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((B, Skv, Hkv, d), generator=g, device=device, dtype=torch.float32)
+    return _cast(q, dtype), _cast(k, dtype), _cast(v, dtype)
+
+
+def workload_inputs(w: Prefill, device="cpu"):
+    return prefill_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.d, w.dtype, w.seed, device)
+
+
+def quantize_rows_int8(x: torch.Tensor):
+    """Per-row symmetric int8 codes over the last axis (see the module docstring)."""
+    x = x.float()
+    absmax = x.abs().amax(dim=-1)
+    scale = absmax / 127.0
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    codes = torch.round(x / safe.unsqueeze(-1)).clamp_(-127, 127)
+    codes = torch.where(scale.unsqueeze(-1) > 0, codes, torch.zeros_like(codes))
+    return codes.to(torch.int8), scale.to(torch.float32)
+
+
+def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False):
+    """q [B,Hq,d] bf16; kq/vq [B,Hkv,Skv,d] int8; k_scale/v_scale [B,Hkv,Skv] fp32.
+
+    Draw order: Q, then for each batch entry K_b [Hkv,Skv,d] and V_b, each
+    quantised as soon as it is drawn (so host memory stays at one slice).
+    With keep_float=True the unquantised fp32 K and V are returned as well.
+    """
+    g = _gen(seed, device)
+    q = torch.randn((B, Hq, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    kq = torch.empty((B, Hkv, Skv, d), dtype=torch.int8, device=device)
+    vq = torch.empty_like(kq)
+    ks = torch.empty((B, Hkv, Skv), dtype=torch.float32, device=device)
+    vs = torch.empty_like(ks)
+    kf = vf = None
+    if keep_float:
+        kf = torch.empty((B, Hkv, Skv, d), dtype=torch.float32, device=device)
+        vf = torch.empty_like(kf)
+    for b in range(B):
+        kb = torch.randn((Hkv, Skv, d), generator=g, device=device, dtype=torch.float32)
+        kq[b], ks[b] = quantize_rows_int8(kb)
+        if keep_float:
+            kf[b] = kb
+        del kb
+        vb = torch.randn((Hkv, Skv, d), generator=g, device=device, dtype=torch.float32)
+        vq[b], vs[b] = quantize_rows_int8(vb)
+        if keep_float:
+            vf[b] = vb
+        del vb
+    if keep_float:
+        return q, kq, ks, vq, vs, kf, vf
+    return q, kq, ks, vq, vs
+
+
+def decode_workload_inputs(w: Decode, device="cpu", keep_float=False):
+    return decode_inputs(w.B, w.Hq, w.Hkv, w.Skv, w.d, w.seed, device, keep_float)
