@@ -1,0 +1,146 @@
+/*
+ * libfattn -- tiled exact attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a DEVICE pointer (memory the caller got
+ * from hipMalloc or a framework allocator on the current HIP device) unless
+ * stated otherwise; all tensors are dense, row-major and contiguous.  The
+ * library allocates and frees nothing, keeps no pointer after a call returns
+ * and holds no per-call state, so calls may be issued from several host
+ * threads at once.  Work is enqueued asynchronously on `stream` (a
+ * hipStream_t passed as void*; NULL is the null stream): buffers must stay
+ * alive until that stream has finished the work.
+ *
+ * Every device pointer must be 16-byte aligned (allocator-returned pointers
+ * are); a misaligned pointer is rejected with FATTN_EINVAL.
+ *
+ * Errors: arguments are validated before any HIP call is made.  On any
+ * FATTN_E* status except FATTN_EHIP nothing has been enqueued and no output
+ * has been written.  FATTN_EHIP reports a failed kernel launch.
+ *
+ * Sources, cited by page title and section:
+ *  [FA-NPU]      "When Transformer meets the Ascend NPU: the memory-slimming
+ *                secret of the FlashAttention operator" (ai6s.net/6a0d479d...)
+ *  [FA-3MOVES]   the ai6s.net article on FlashAttention's three moves and CANN
+ *                8.0 -> 8.5 (ai6s.net/6a0d6a93...)
+ *  [FA-VARIANTS] "The FlashAttention variant family: GQA, MQA and sparse
+ *                attention, how to choose" (ai6s.net/6a17bd37...)
+ */
+#ifndef FATTN_H
+#define FATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define FATTN_API __attribute__((visibility("default")))
+#else
+#define FATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call that can fail. */
+typedef enum {
+  FATTN_OK = 0,
+  FATTN_EINVAL = -1,      /* a NULL or misaligned pointer, a size < 1,
+                             Hq % Hkv != 0, a
+                             non-finite scale, causal not 0/1, window < 0,
+                             window > 0 without causal, num_splits < 0, or a
+                             tensor too large to index */
+  FATTN_EUNSUPPORTED = -2, /* head_dim or dtype outside what the kernels cover */
+  FATTN_EWORKSPACE = -3,  /* workspace NULL or smaller than the size query */
+  FATTN_EHIP = -4         /* the HIP runtime refused a kernel launch */
+} fattn_status;
+
+/* Element type of q, k, v and o in fattn_fwd. */
+typedef enum {
+  FATTN_F32 = 0, /* float32 in and out, fp32 arithmetic */
+  FATTN_BF16 = 1 /* bfloat16 in and out, bf16 matrix products with fp32
+                    accumulation and an fp32 softmax */
+} fattn_dtype;
+
+/*
+ * Exact attention forward (prefill):
+ *   o = softmax(scale * q k^T + mask) v,
+ * the definition in [FA-NPU] (section on why attention is so memory-hungry)
+ * computed tile by tile with an online softmax ([FA-NPU] tiling section;
+ * [FA-3MOVES] moves 1 and 2): each query tile streams key/value tiles, keeps
+ * a running row max and row sum, rescales its accumulator, and never writes
+ * the Sq x Skv score matrix to memory.
+ *
+ * q    [B, Sq, Hq, d]   (batch, sequence, heads, head_dim: the order of the
+ *                        usage section of [FA-NPU])
+ * k, v [B, Skv, Hkv, d]
+ * o    [B, Sq, Hq, d]   output, same shape and dtype as q
+ * lse  [B, Hq, Sq] fp32 output or NULL: natural log of the row's sum of
+ *      exp(scale * q.k) over visible keys (the row statistic the backward
+ *      pass recomputes from, [FA-NPU] recomputation section); -inf for a row
+ *      with no visible key (its o row is then 0).
+ * Hq must be a multiple of Hkv; query head h reads kv head h / (Hq/Hkv), the
+ *      head sharing of GQA/MQA ([FA-VARIANTS] GQA section), done in the
+ *      kernel without copying k or v.
+ * scale: any finite value (1/sqrt(d) in the pages' examples).
+ * causal: 0 or 1.  With causal = 1 key j is visible to query i iff
+ *      j <= i + (Skv - Sq) (aligned to the last query; the pages' examples
+ *      have Sq = Skv, where this is the usual lower triangle).
+ * window: 0 = none; W > 0 (needs causal = 1) keeps the W keys
+ *      i + (Skv - Sq) - W < j <= i + (Skv - Sq), the query's own position
+ *      included ([FA-VARIANTS] local window attention section).
+ * d: 64 or 128.  dtype: a fattn_dtype.
+ */
+FATTN_API int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int Sq, int Skv, int d,
+              float scale, int causal, int window, int dtype, void* stream);
+
+/*
+ * Decode over an int8 KV cache ([FA-3MOVES] move 3: the cache stays
+ * compressed and is used as is).  One new query token per sequence attends
+ * to all Skv cached tokens.  The cache holds per (token, kv head) an int8 row
+ * of d codes and one fp32 scale; the key/value the attention sees is
+ * code * scale.  The kernel reads the codes from HBM and converts them in
+ * registers, folding the scales into the scores and the probabilities.
+ * The keys are cut into splits processed in parallel, each producing a
+ * partial (o_s, lse_s) in the workspace; a second kernel merges them by
+ * log-sum-exp (the local-max-and-sum correction of the [FA-NPU] tiling
+ * section applied across splits).
+ *
+ * q          [B, Hq, d] bf16          (the [B, 1, Hq, d] query of the new token)
+ * kq, vq     [B, Hkv, Skv, d] int8    (head-major cache: one contiguous stream
+ *                                      per (b, kv head))
+ * k_scale, v_scale [B, Hkv, Skv] fp32
+ * o          [B, Hq, d] bf16 output;  lse [B, Hq] fp32 output or NULL
+ * num_splits 0 = automatic; otherwise the requested number of key splits per
+ *            (b, kv head) (the library may use fewer so that none is empty)
+ * workspace  device scratch of at least fattn_decode_workspace_size(...)
+ *            bytes for the same arguments; its contents on entry do not matter
+ *            and on return are undefined.  Concurrent calls need separate
+ *            workspaces.
+ * d: 64 or 128.  Hq % Hkv == 0.
+ */
+FATTN_API int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_scale,
+                      const int8_t* vq, const float* v_scale, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Skv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Number of key splits fattn_decode_int8 will use for these arguments
+ * (>= 1), or a negative fattn_status if they are invalid.  Host only. */
+FATTN_API int fattn_decode_num_splits(int B, int Hq, int Hkv, int Skv, int d, int num_splits);
+
+/* Workspace bytes fattn_decode_int8 needs for these arguments, 0 if they are
+ * invalid.  Host only; pure function of its arguments. */
+FATTN_API size_t fattn_decode_workspace_size(int B, int Hq, int Hkv, int Skv, int d, int num_splits);
+
+/* Static, NUL-terminated description of a status code.  Host only. */
+FATTN_API const char* fattn_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch.  Host only. */
+FATTN_API int fattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATTN_H */

@@ -1,0 +1,171 @@
+"""The C-ABI boundary on the CPU: library loads, exports what include/fattn.h
+declares, and rejects every invalid argument before touching a device.
+
+Invalid calls use fake (but aligned) device addresses; validation must reject
+them before any HIP call.  Those cases only run where no GPU is visible, so a
+validation bug can never send a fake pointer to a real device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import tiled_exact_attention_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fattn.h")
+
+FATTN_OK, FATTN_EINVAL, FATTN_EUNSUPPORTED, FATTN_EWORKSPACE = 0, -1, -2, -3
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FATTN_API\s+[\w\s\*]+?\b(fattn_\w+)\s*\(", text)))
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake device pointers are only passed where no GPU can be reached")
+
+
+def test_library_is_built_and_loads():
+    lib = fa.load()
+    assert os.path.exists(fa.library_path())
+    assert lib is fa.load()
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert names == sorted(["fattn_fwd", "fattn_decode_int8", "fattn_decode_num_splits",
+                            "fattn_decode_workspace_size", "fattn_status_string", "fattn_version"])
+    lib = ctypes.CDLL(fa.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+        assert hasattr(fa, n), n  # the binding mirrors the C names
+
+
+def test_only_declared_symbols_are_exported():
+    # internal launchers are hidden; nothing but the C ABI is visible
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    mine = {s for s in syms if "fattn" in s}
+    assert mine == set(_declared_functions())
+
+
+def test_version_and_status_strings():
+    assert fa.fattn_version() == 10000
+    assert fa.fattn_status_string(0) == "ok"
+    for st in (FATTN_EINVAL, FATTN_EUNSUPPORTED, FATTN_EWORKSPACE, -4):
+        assert fa.fattn_status_string(st) not in ("ok", "unknown status")
+    assert fa.fattn_status_string(12345) == "unknown status"
+
+
+def _plan(Skv, req, B=1, Hkv=1):
+    """Split plan the header documents: chunks of whole 64-token tiles, no empty split."""
+    if req == 0:
+        req = min(max(-(-8192 // (B * Hkv)), 1), -(-Skv // 256), 1024)
+    req = min(req, Skv)
+    chunk = -(-Skv // req)
+    chunk = -(-chunk // 64) * 64
+    return -(-Skv // chunk), chunk
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Skv,d,req", [
+    (32, 32, 8, 32768, 128, 0), (1, 4, 1, 1, 64, 0), (2, 8, 2, 1000, 128, 7),
+    (1, 1, 1, 65, 64, 3), (3, 6, 3, 4097, 128, 16), (1, 2, 2, 64, 64, 64), (4, 4, 4, 70000, 64, 0)])
+def test_split_plan_and_workspace_size(B, Hq, Hkv, Skv, d, req):
+    n = fa.decode_num_splits(B, Hq, Hkv, Skv, d, req)
+    want_n, chunk = _plan(Skv, req, B, Hkv)
+    assert n == want_n
+    assert (n - 1) * chunk < Skv <= n * chunk  # every split non-empty
+    rows = B * Hq * n
+    want_ws = -(-(rows * d * 4) // 256) * 256 + rows * 4
+    assert fa.decode_workspace_size(B, Hq, Hkv, Skv, d, req) == want_ws
+
+
+def test_size_queries_reject_bad_arguments():
+    assert fa.fattn_decode_num_splits(1, 3, 2, 10, 64, 0) == FATTN_EINVAL
+    assert fa.fattn_decode_num_splits(1, 2, 2, 10, 96, 0) == FATTN_EUNSUPPORTED
+    assert fa.fattn_decode_num_splits(1, 2, 2, 0, 64, 0) == FATTN_EINVAL
+    assert fa.fattn_decode_num_splits(1, 2, 2, 10, 64, -1) == FATTN_EINVAL
+    assert fa.fattn_decode_workspace_size(1, 3, 2, 10, 64, 0) == 0
+
+
+P = 0x10000  # fake aligned device address
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=2, Sq=8, Skv=8, d=64, scale=0.125,
+             causal=0, window=0, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fattn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                        a["Sq"], a["Skv"], a["d"], a["scale"], a["causal"], a["window"],
+                        a["dtype"], a["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), FATTN_EINVAL), (dict(k=None), FATTN_EINVAL), (dict(v=None), FATTN_EINVAL),
+    (dict(o=None), FATTN_EINVAL), (dict(q=P + 8), FATTN_EINVAL), (dict(o=P + 2), FATTN_EINVAL),
+    (dict(B=0), FATTN_EINVAL), (dict(Hq=0), FATTN_EINVAL), (dict(Hkv=0), FATTN_EINVAL),
+    (dict(Sq=0), FATTN_EINVAL), (dict(Skv=-1), FATTN_EINVAL), (dict(d=0), FATTN_EINVAL),
+    (dict(Hq=3, Hkv=2), FATTN_EINVAL), (dict(scale=math.inf), FATTN_EINVAL),
+    (dict(scale=math.nan), FATTN_EINVAL), (dict(causal=2), FATTN_EINVAL),
+    (dict(window=-1, causal=1), FATTN_EINVAL), (dict(window=4, causal=0), FATTN_EINVAL),
+    (dict(d=96), FATTN_EUNSUPPORTED), (dict(d=256), FATTN_EUNSUPPORTED),
+    (dict(dtype=2), FATTN_EUNSUPPORTED), (dict(dtype=-1), FATTN_EUNSUPPORTED),
+    (dict(B=1 << 20, Hq=1 << 10, Hkv=1, Sq=1 << 12, Skv=4), FATTN_EINVAL),
+])
+def test_fwd_rejects_before_any_device_work(kw, want):
+    assert _fwd(**kw) == want
+
+
+def _dec(**kw):
+    a = dict(q=P, kq=P, ks=P, vq=P, vs=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Skv=100, d=128,
+             scale=0.1, num_splits=0, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return fa.fattn_decode_int8(a["q"], a["kq"], a["ks"], a["vq"], a["vs"], a["o"], a["lse"],
+                                a["B"], a["Hq"], a["Hkv"], a["Skv"], a["d"], a["scale"],
+                                a["num_splits"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), FATTN_EINVAL), (dict(kq=None), FATTN_EINVAL), (dict(ks=None), FATTN_EINVAL),
+    (dict(vq=None), FATTN_EINVAL), (dict(vs=None), FATTN_EINVAL), (dict(o=None), FATTN_EINVAL),
+    (dict(ks=P + 4), FATTN_EINVAL), (dict(lse=P + 4), FATTN_EINVAL),
+    (dict(B=0), FATTN_EINVAL), (dict(Hq=3), FATTN_EINVAL), (dict(Skv=0), FATTN_EINVAL),
+    (dict(scale=-math.inf), FATTN_EINVAL), (dict(num_splits=-2), FATTN_EINVAL),
+    (dict(d=32), FATTN_EUNSUPPORTED),
+    (dict(ws=None), FATTN_EWORKSPACE), (dict(ws_bytes=16), FATTN_EWORKSPACE),
+    (dict(ws=P + 8), FATTN_EWORKSPACE),
+])
+def test_decode_rejects_before_any_device_work(kw, want):
+    assert _dec(**kw) == want
+
+
+@no_gpu_only
+def test_decode_workspace_boundary_is_exact():
+    need = fa.decode_workspace_size(1, 4, 2, 100, 128, 0)
+    assert _dec(ws_bytes=need - 1) == FATTN_EWORKSPACE
+
+
+def test_torch_wrappers_reject_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)
+    with pytest.raises(TypeError):
+        fa.fwd(q.half(), q.half(), q.half())

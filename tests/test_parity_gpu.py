@@ -1,0 +1,264 @@
+"""GPU parity: libfattn (through its C ABI) against the fp64 oracle.
+
+Small and odd shapes are compared element by element over every output; the
+full-size workloads (run exactly as the benchmark launches them) are compared
+on sampled rows the oracle computes one by one, plus properties that hold at
+any size (every element finite and written, each output row inside the range
+of the values it averages, bitwise repeatability).
+
+Tolerances (fixed for this build): fp32 inputs max-abs 1e-5 on o and lse;
+bf16 inputs max-abs 2e-2 and mean-abs 2e-3 on o, max-abs 1e-3 on lse.  The
+decode output is bf16 and uses the bf16 bounds.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_exact_attention_amd as fa
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_MAX, BF16_MEAN, BF16_LSE = 2e-2, 2e-3, 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _np64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def _check_bf16(o_gpu, o_ref, lse_gpu, lse_ref, what):
+    err = np.abs(o_gpu - o_ref)
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite output"
+    assert err.max() <= BF16_MAX, f"{what}: max-abs {err.max():.3e}"
+    assert err.mean() <= BF16_MEAN, f"{what}: mean-abs {err.mean():.3e}"
+    if lse_ref is not None:
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(fin, np.isfinite(lse_gpu)), f"{what}: lse finiteness differs"
+        if fin.any():
+            le = np.abs(lse_gpu[fin] - lse_ref[fin]).max()
+            assert le <= BF16_LSE, f"{what}: lse max-abs {le:.3e}"
+    return err.max(), err.mean()
+
+
+def _run_fwd(q, k, v, causal, window, scale, dev):
+    o = torch.full_like(q, float("nan"), device=dev)  # poison: every element must be written
+    o, lse = fa.fwd(q, k, v, causal=causal, window=window, scale=scale, return_lse=True, out=o)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ----------------------------------------------------------------- fp32 path
+
+def test_tiny_fp32_workload(cuda_device):
+    w = W.TINY_F32
+    _say(f"case: {w.name}")
+    q, k, v = W.workload_inputs(w)
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale)
+    o, lse = _run_fwd(q.to(cuda_device), k.to(cuda_device), v.to(cuda_device), w.causal, w.window,
+                      w.scale, cuda_device)
+    err = np.abs(_np64(o) - o_ref).max()
+    lerr = np.abs(_np64(lse) - lse_ref).max()
+    _say(f"  max-abs o {err:.3e}, lse {lerr:.3e}")
+    assert err <= F32_TOL and lerr <= F32_TOL
+
+
+F32_CASES = [
+    # B, Hq, Hkv, Sq, Skv, d, causal, window, scale
+    (1, 2, 2, 1, 1, 64, False, 0, None),
+    (2, 4, 2, 17, 17, 64, True, 0, None),
+    (1, 3, 1, 129, 129, 128, True, 0, None),
+    (1, 2, 1, 65, 200, 64, True, 0, None),
+    (1, 2, 2, 200, 65, 128, True, 0, None),
+    (1, 4, 4, 127, 127, 64, True, 5, None),
+    (1, 2, 1, 100, 100, 128, False, 0, -0.3),
+    (1, 2, 2, 70, 70, 64, True, 1000, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[str(c) for c in F32_CASES])
+def test_fp32_odd_shapes(case, cuda_device):
+    B, Hq, Hkv, Sq, Skv, d, causal, window, scale = case
+    _say(f"case fp32 {case}")
+    g = torch.Generator().manual_seed(100 + sum(case[:6]))
+    q = torch.randn(B, Sq, Hq, d, generator=g)
+    k = torch.randn(B, Skv, Hkv, d, generator=g)
+    v = torch.randn(B, Skv, Hkv, d, generator=g)
+    s = 1 / math.sqrt(d) if scale is None else scale
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal=causal, window=window, scale=s)
+    o, lse = _run_fwd(q.to(cuda_device), k.to(cuda_device), v.to(cuda_device), causal, window, s,
+                      cuda_device)
+    o, lse = _np64(o), _np64(lse)
+    assert np.all(np.isfinite(o))
+    assert np.abs(o - o_ref).max() <= F32_TOL
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.abs(lse[fin] - lse_ref[fin]).max() <= F32_TOL if fin.any() else True
+
+
+# ----------------------------------------------------------------- bf16 path
+
+BF16_CASES = [
+    # B, Hq, Hkv, Sq, Skv, d, causal, window, scale
+    (1, 1, 1, 1, 1, 64, False, 0, None),
+    (1, 2, 2, 17, 17, 128, True, 0, None),
+    (2, 4, 4, 128, 128, 128, True, 0, None),
+    (1, 2, 2, 129, 129, 64, True, 0, None),
+    (1, 2, 2, 300, 300, 128, False, 0, None),
+    (1, 8, 2, 257, 257, 128, True, 0, None),      # GQA G=4
+    (1, 16, 2, 100, 100, 64, True, 0, None),      # GQA G=8
+    (1, 29, 1, 70, 70, 64, True, 0, None),        # odd group (G=29 -> 1 head per chunk)
+    (1, 232, 1, 40, 40, 64, True, 0, None),       # MQA, 232 heads
+    (1, 64, 1, 20, 20, 128, True, 0, None),       # 32-head chunks
+    (1, 6, 3, 97, 250, 128, True, 0, None),       # Sq < Skv (continuation)
+    (1, 2, 1, 250, 97, 64, True, 0, None),        # Sq > Skv: leading rows see nothing
+    (1, 4, 2, 333, 333, 128, True, 63, None),     # window
+    (1, 8, 1, 300, 300, 64, True, 1, None),       # window of one key
+    (1, 2, 2, 200, 200, 128, True, 512, None),    # window >= S
+    (1, 4, 2, 150, 150, 64, True, 0, -0.2),       # negative scale
+    (1, 2, 2, 90, 90, 128, True, 0, 0.0),         # zero scale: uniform rows
+    (2, 8, 8, 64, 1000, 64, False, 0, None),      # non-causal, long keys
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=[str(c) for c in BF16_CASES])
+def test_bf16_odd_shapes(case, cuda_device):
+    B, Hq, Hkv, Sq, Skv, d, causal, window, scale = case
+    _say(f"case bf16 {case}")
+    q, k, v = W.prefill_inputs(B, Hq, Hkv, Sq, Skv, d, "bf16", seed=200 + sum(case[:6]))
+    s = 1 / math.sqrt(d) if scale is None else scale
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal=causal, window=window, scale=s)
+    o, lse = _run_fwd(q.to(cuda_device), k.to(cuda_device), v.to(cuda_device), causal, window, s,
+                      cuda_device)
+    mx, mean = _check_bf16(_np64(o), o_ref, _np64(lse), lse_ref, str(case))
+    _say(f"  max-abs {mx:.3e} mean-abs {mean:.3e}")
+
+
+def _sample_rows(B, Hq, Sq, n, seed):
+    """(b, h, i) rows: first/last positions, tile edges, and random ones."""
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 129, 511, 512, 1023, Sq // 2, Sq - 2, Sq - 1]
+    rows = []
+    for i in edges:
+        if 0 <= i < Sq:
+            rows.append((rng.integers(B), rng.integers(Hq), i))
+    for h in range(Hq):  # every head at least once
+        rows.append((rng.integers(B), h, rng.integers(Sq)))
+    while len(rows) < n:
+        rows.append((rng.integers(B), rng.integers(Hq), rng.integers(Sq)))
+    return np.array(rows, dtype=np.int64)
+
+
+FULL = [W.MHA_CAUSAL, W.GQA_CAUSAL, W.MQA_CAUSAL, W.MQA_WINDOW]
+
+
+@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
+def test_full_size_prefill_sampled(w, cuda_device):
+    _say(f"case: {w.name}")
+    q, k, v = W.workload_inputs(w)
+    qd, kd, vd = q.to(cuda_device), k.to(cuda_device), v.to(cuda_device)
+    o, lse = _run_fwd(qd, kd, vd, w.causal, w.window, w.scale, cuda_device)
+    o2, lse2 = _run_fwd(qd, kd, vd, w.causal, w.window, w.scale, cuda_device)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "not bitwise repeatable"
+    assert bool(torch.isfinite(o).all()), "non-finite (or unwritten) output"
+    assert bool(torch.isfinite(lse).all())
+    rows = _sample_rows(w.B, w.Hq, w.Sq, 384, seed=w.seed)
+    o_ref, lse_ref = oracle.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale, rows=rows)
+    o_np = o.float().cpu().numpy()
+    l_np = lse.cpu().numpy()
+    o_got = np.stack([o_np[b, i, h] for b, h, i in rows]).astype(np.float64)
+    l_got = np.array([l_np[b, h, i] for b, h, i in rows], dtype=np.float64)
+    mx, mean = _check_bf16(o_got, o_ref, l_got, lse_ref, w.name)
+    _say(f"  sampled {len(rows)} rows: max-abs {mx:.3e} mean-abs {mean:.3e}")
+    # any size: each output row is a convex combination of the visible V rows
+    vmax = v.float().abs().amax().item()
+    assert float(o.float().abs().amax()) <= vmax * (1 + 2 ** -7) + 1e-6
+
+
+# -------------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    # B, Hq, Hkv, Skv, d, num_splits
+    (1, 1, 1, 1, 64, 0),
+    (2, 4, 1, 7, 128, 0),
+    (1, 8, 2, 64, 128, 1),
+    (1, 8, 2, 65, 64, 0),
+    (2, 8, 8, 1000, 128, 3),
+    (1, 32, 8, 4097, 128, 0),
+    (1, 20, 1, 333, 64, 4),       # 20 heads per kv head: two head chunks
+    (1, 40, 2, 129, 128, 2),
+    (3, 6, 3, 2050, 64, 7),
+    (1, 4, 4, 999, 128, 1000),     # more splits requested than tiles
+]
+
+
+def _decode_case(B, Hq, Hkv, Skv, d, num_splits, seed, dev, scale=None):
+    q, kq, ks, vq, vs = W.decode_inputs(B, Hq, Hkv, Skv, d, seed=seed)
+    s = 1 / math.sqrt(d) if scale is None else scale
+    o_ref, lse_ref = oracle.decode_int8(q, kq, ks, vq, vs, scale=s)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    o, lse = fa.decode_int8(q.to(dev), kq.to(dev), ks.to(dev), vq.to(dev), vs.to(dev), scale=s,
+                            num_splits=num_splits, return_lse=True, out=out)
+    torch.cuda.synchronize()
+    return _np64(o), _np64(lse), o_ref, lse_ref
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[str(c) for c in DECODE_CASES])
+def test_decode_odd_shapes(case, cuda_device):
+    _say(f"case decode {case}")
+    o, lse, o_ref, lse_ref = _decode_case(*case, seed=300 + sum(case), dev=cuda_device)
+    mx, mean = _check_bf16(o, o_ref, lse, lse_ref, str(case))
+    _say(f"  max-abs {mx:.3e} mean-abs {mean:.3e}")
+
+
+def test_decode_negative_and_zero_scale(cuda_device):
+    for s in (-0.15, 0.0):
+        _say(f"case decode scale {s}")
+        o, lse, o_ref, lse_ref = _decode_case(2, 8, 2, 300, 128, 0, seed=7, dev=cuda_device, scale=s)
+        _check_bf16(o, o_ref, lse, lse_ref, f"scale {s}")
+
+
+def test_decode_split_count_does_not_change_the_result(cuda_device):
+    _say("case decode split invariance")
+    B, Hq, Hkv, Skv, d = 2, 8, 2, 3000, 128
+    q, kq, ks, vq, vs = [t.to(cuda_device) for t in W.decode_inputs(B, Hq, Hkv, Skv, d, seed=9)]
+    outs = []
+    for ns in (1, 2, 5, 47):
+        o, lse = fa.decode_int8(q, kq, ks, vq, vs, num_splits=ns, return_lse=True)
+        outs.append((o.float(), lse))
+    torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert float((o - outs[0][0]).abs().max()) <= 2 ** -7
+        assert float((lse - outs[0][1]).abs().max()) <= 1e-4
+
+
+def test_full_size_decode_sampled(cuda_device):
+    w = W.INT8_DECODE
+    _say(f"case: {w.name}")
+    q, kq, ks, vq, vs = W.decode_workload_inputs(w, device=cuda_device)
+    o, lse = fa.decode_int8(q, kq, ks, vq, vs, scale=w.scale, return_lse=True)
+    o2, lse2 = fa.decode_int8(q, kq, ks, vq, vs, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "not bitwise repeatable"
+    assert bool(torch.isfinite(o.float()).all())
+    rng = np.random.default_rng(w.seed)
+    rows = np.array([(0, 0), (w.B - 1, w.Hq - 1)] +
+                    [(rng.integers(w.B), rng.integers(w.Hq)) for _ in range(46)], dtype=np.int64)
+    qc, kqc, ksc, vqc, vsc = (t.cpu() for t in (q, kq, ks, vq, vs))
+    o_ref, lse_ref = oracle.decode_int8(qc, kqc, ksc, vqc, vsc, scale=w.scale, rows=rows)
+    o_np, l_np = _np64(o), _np64(lse)
+    o_got = np.stack([o_np[b, h] for b, h in rows])
+    l_got = np.array([l_np[b, h] for b, h in rows])
+    mx, mean = _check_bf16(o_got, o_ref, l_got, lse_ref, w.name)
+    _say(f"  sampled {len(rows)} rows: max-abs {mx:.3e} mean-abs {mean:.3e}")

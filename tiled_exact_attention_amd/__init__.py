@@ -1,0 +1,29 @@
+"""libfattn: tiled exact attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI declared in ``include/fattn.h``.  Every
+step of the computation runs in the HIP kernels of ``libfattn.so``; this
+package only checks tensors, allocates outputs with torch (device memory and
+streams are all torch is used for) and passes raw pointers.  There is no
+fallback: if the library is not built, every call raises.
+
+    import tiled_exact_attention_amd as fa
+    o = fa.fwd(q, k, v, causal=True)                 # q [B,S,Hq,d], k/v [B,S,Hkv,d]
+    o, lse = fa.decode_int8(q, kq, ks, vq, vs, return_lse=True)
+"""
+from ._binding import (  # noqa: F401
+    FATTN_BF16,
+    FATTN_F32,
+    FattnError,
+    decode_int8,
+    decode_num_splits,
+    decode_workspace_size,
+    fattn_decode_int8,
+    fattn_decode_num_splits,
+    fattn_decode_workspace_size,
+    fattn_fwd,
+    fattn_status_string,
+    fattn_version,
+    fwd,
+    library_path,
+    load,
+)

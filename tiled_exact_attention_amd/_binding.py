@@ -1,0 +1,211 @@
+"""ctypes marshalling for libfattn (argument checks and pointers only).
+
+The raw entry points ``fattn_fwd``, ``fattn_decode_int8``,
+``fattn_decode_workspace_size``, ``fattn_decode_num_splits``,
+``fattn_status_string`` and ``fattn_version`` have the C names and take plain
+integers (device pointers as ints, streams as ints or None).  ``fwd`` and
+``decode_int8`` accept torch tensors, allocate the outputs and call them on
+the current torch stream of the tensors' device.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfattn.so")
+_lib = None
+
+FATTN_F32 = 0
+FATTN_BF16 = 1
+
+
+class FattnError(RuntimeError):
+    """A libfattn call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fattn_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Loads libfattn.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it first with "
+                "`python -m tiled_exact_attention_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fattn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                  f32, i32, i32, i32, vp]
+        lib.fattn_fwd.restype = i32
+        lib.fattn_decode_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                          f32, i32, vp, sz, vp]
+        lib.fattn_decode_int8.restype = i32
+        lib.fattn_decode_num_splits.argtypes = [i32] * 6
+        lib.fattn_decode_num_splits.restype = i32
+        lib.fattn_decode_workspace_size.argtypes = [i32] * 6
+        lib.fattn_decode_workspace_size.restype = sz
+        lib.fattn_status_string.argtypes = [i32]
+        lib.fattn_status_string.restype = ctypes.c_char_p
+        lib.fattn_version.argtypes = []
+        lib.fattn_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+# ---------------------------------------------------------------- raw C names
+
+def fattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, scale, causal, window, dtype, stream) -> int:
+    return load().fattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, scale, causal, window,
+                            dtype, stream)
+
+
+def fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
+                      num_splits, workspace, workspace_bytes, stream) -> int:
+    return load().fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d,
+                                    scale, num_splits, workspace, workspace_bytes, stream)
+
+
+def fattn_decode_num_splits(B, Hq, Hkv, Skv, d, num_splits) -> int:
+    return load().fattn_decode_num_splits(B, Hq, Hkv, Skv, d, num_splits)
+
+
+def fattn_decode_workspace_size(B, Hq, Hkv, Skv, d, num_splits) -> int:
+    return load().fattn_decode_workspace_size(B, Hq, Hkv, Skv, d, num_splits)
+
+
+def fattn_status_string(status: int) -> str:
+    return load().fattn_status_string(int(status)).decode()
+
+
+def fattn_version() -> int:
+    return load().fattn_version()
+
+
+# ------------------------------------------------------------- torch wrappers
+
+def _check(t, name, dtype, ndim, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_of(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | None = None,
+        return_lse: bool = False, out=None):
+    """Exact attention o = softmax(scale*q@k^T + mask) @ v (see fattn_fwd).
+
+    q [B, Sq, Hq, d], k/v [B, Skv, Hkv, d], all float32 or all bfloat16,
+    contiguous, on one GPU.  Returns o shaped like q (and lse [B, Hq, Sq] fp32).
+    """
+    import torch
+    dtype = q.dtype
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _check(q, "q", dtype, 4)
+    _check(k, "k", dtype, 4, q.device)
+    _check(v, "v", dtype, 4, q.device)
+    B, Sq, Hq, d = q.shape
+    Bk, Skv, Hkv, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", dtype, 4, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    with torch.cuda.device(q.device):
+        st = fattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                       lse.data_ptr() if lse is not None else None,
+                       B, Hq, Hkv, Sq, Skv, d, float(scale), int(bool(causal)), int(window),
+                       FATTN_F32 if dtype == torch.float32 else FATTN_BF16, _stream_of(q.device))
+    if st != 0:
+        raise FattnError(st, "fattn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def decode_num_splits(B, Hq, Hkv, Skv, d, num_splits=0) -> int:
+    n = fattn_decode_num_splits(B, Hq, Hkv, Skv, d, num_splits)
+    if n < 1:
+        raise FattnError(n, "fattn_decode_num_splits")
+    return n
+
+
+def decode_workspace_size(B, Hq, Hkv, Skv, d, num_splits=0) -> int:
+    n = fattn_decode_workspace_size(B, Hq, Hkv, Skv, d, num_splits)
+    if n == 0:
+        raise FattnError(-1, "fattn_decode_workspace_size")
+    return n
+
+
+def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_splits: int = 0,
+                workspace=None, return_lse: bool = False, out=None):
+    """Decode attention of one token over an int8 KV cache (see fattn_decode_int8).
+
+    q [B, Hq, d] bf16; kq/vq [B, Hkv, Skv, d] int8; k_scale/v_scale [B, Hkv, Skv] fp32.
+    workspace: optional uint8 GPU tensor of at least decode_workspace_size(...)
+    bytes (allocated here if None).  Returns o [B, Hq, d] bf16 (and lse [B, Hq]).
+    """
+    import torch
+    _check(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _check(kq, "kq", torch.int8, 4, dev)
+    _check(vq, "vq", torch.int8, 4, dev)
+    _check(k_scale, "k_scale", torch.float32, 3, dev)
+    _check(v_scale, "v_scale", torch.float32, 3, dev)
+    B, Hq, d = q.shape
+    Bk, Hkv, Skv, dk = kq.shape
+    if Bk != B or dk != d or tuple(vq.shape) != tuple(kq.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kq {tuple(kq.shape)}, vq {tuple(vq.shape)}")
+    if tuple(k_scale.shape) != (B, Hkv, Skv) or tuple(v_scale.shape) != (B, Hkv, Skv):
+        raise ValueError("k_scale and v_scale must be [B, Hkv, Skv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_size(B, Hq, Hkv, Skv, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    with torch.cuda.device(dev):
+        st = fattn_decode_int8(q.data_ptr(), kq.data_ptr(), k_scale.data_ptr(), vq.data_ptr(),
+                               v_scale.data_ptr(), out.data_ptr(),
+                               lse.data_ptr() if lse is not None else None,
+                               B, Hq, Hkv, Skv, d, float(scale), int(num_splits),
+                               workspace.data_ptr(), ws_bytes, _stream_of(dev))
+    if st != 0:
+        raise FattnError(st, "fattn_decode_int8")
+    return (out, lse) if return_lse else out

@@ -1,0 +1,80 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// transposed LDS reads and packed conversions.
+//
+// Lane layouts (checked on gfx950 with an in-bounds probe):
+//  * v_mfma_f32_32x32x16_bf16: A[i][k] in lane i%32 (i = l%32), k = 8*(l/32)+e;
+//    B[k][j] in lane j = l%32, k = 8*(l/32)+e; C[i][j] in lane j = l%32,
+//    register r holds row i = 8*(r/4) + 4*(l/32) + r%4.
+//  * v_mfma_f32_16x16x32_bf16: A[i][k] in lane i = l%16, k = 8*(l/16)+e;
+//    B[k][j] in lane j = l%16, k = 8*(l/16)+e; C[i][j] in lane j = l%16,
+//    register r holds row i = 4*(l/16) + r.
+//  * ds_read_b64_tr_b16: within each group of 16 lanes, lane t receives
+//    element t%4 of the 4-element (8-byte) pieces addressed by lanes
+//    t/4 + 4e, e = 0..3.  If lane s of the group addresses row R0 + s/4,
+//    columns C0 + 4*(s%4) .. +3 of a row-major 16-bit matrix, lane t gets
+//    column C0 + t of rows R0 .. R0+3.
+//  * ds_read_b64_tr_b8: within each group of 16 lanes, lane t receives byte
+//    t%8 of the 8-byte pieces addressed by lanes 2e + t/8, e = 0..7.  If lane
+//    s addresses row rho(s/2), columns C0 + 8*(s%2) .. +7 of a row-major byte
+//    matrix, lane t gets column C0 + t of rows rho(0) .. rho(7).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#define FATTN_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 16-bit LDS read (see the layout note above); p is an LDS address.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(FATTN_LDS(i16x4, const_cast<void*>(p)));
+}
+
+// Transposed 8-bit LDS read (see the layout note above); p is an LDS address.
+__device__ __forceinline__ i32x2 lds_read_tr8(const void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(FATTN_LDS(i32x2, const_cast<void*>(p)));
+}
+
+// Round-to-nearest-even fp32 -> bf16 of 8 values.
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
+                                            float a4, float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+// 8 signed bytes (two dwords, byte 0 of lo first) -> 8 bf16 (exact: |x| <= 128).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  return to_bf16x8((float)(int8_t)(lo), (float)(int8_t)(lo >> 8),
+                   (float)(int8_t)(lo >> 16), (float)(int8_t)(lo >> 24),
+                   (float)(int8_t)(hi), (float)(int8_t)(hi >> 8),
+                   (float)(int8_t)(hi >> 16), (float)(int8_t)(hi >> 24));
+}
+
+__device__ __forceinline__ i16x8 concat_i16x4(const i16x4& a, const i16x4& b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float wave_max_xor(float x, int mask) {
+  return fmaxf(x, __shfl_xor(x, mask));
+}
+
+}  // namespace fattn

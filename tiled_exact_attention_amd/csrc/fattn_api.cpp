@@ -1,0 +1,163 @@
+// C-ABI layer of libfattn: argument validation, split planning, dispatch.
+//
+// Validation runs before any HIP call, so an invalid call enqueues nothing and
+// writes nothing, and this part is testable on a machine without a GPU.
+#include "../../include/fattn.h"
+#include "launch.h"
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+// Largest element count a tensor may have: offsets are computed in 64-bit
+// arithmetic and must not overflow when multiplied by the element size.
+constexpr int64_t kMaxElements = int64_t(1) << 56;
+
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
+  // a*b*c*d <= kMaxElements, with every factor >= 1
+  int64_t p = a;
+  for (int64_t f : {b, c, d}) {
+    if (p > kMaxElements / f) return false;
+    p *= f;
+  }
+  return true;
+}
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// Kernels use 16-byte vector loads/stores on every tensor.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Automatic split count: enough single-wave (b, kv head, split) work items to
+// give each of the 256 compute units about 32 waves, with each split long
+// enough (>= 256 tokens) that its partial write and the merge stay small
+// beside the cache stream.  A pure function of the arguments (no device
+// query), so the workspace size is known on the host before any device work.
+int auto_splits(int B, int Hkv, int Skv) {
+  const int64_t target_items = 8192;
+  const int64_t streams = int64_t(B) * Hkv;
+  int64_t want = (target_items + streams - 1) / streams;
+  const int64_t max_by_len = (int64_t(Skv) + 255) / 256;
+  if (want > max_by_len) want = max_by_len;
+  if (want < 1) want = 1;
+  if (want > 1024) want = 1024;
+  return int(want);
+}
+
+// Resolves the split plan: chunk = tokens per split (a multiple of the kernel
+// tile), nsplit = number of non-empty splits.
+void plan_splits(int B, int Hkv, int Skv, int requested, int* nsplit, int* chunk) {
+  int want = requested > 0 ? requested : auto_splits(B, Hkv, Skv);
+  if (want > Skv) want = Skv;
+  int64_t c = (int64_t(Skv) + want - 1) / want;
+  c = (c + fattn::kDecodeTile - 1) / fattn::kDecodeTile * fattn::kDecodeTile;
+  *chunk = int(c);
+  *nsplit = int((int64_t(Skv) + c - 1) / c);
+}
+
+int validate_decode(const void* q, const void* kq, const void* ks, const void* vq, const void* vs,
+                    const void* o, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                    int num_splits, bool check_pointers) {
+  if (check_pointers && (!q || !kq || !ks || !vq || !vs || !o)) return FATTN_EINVAL;
+  if (check_pointers && !(aligned16(q) && aligned16(kq) && aligned16(ks) && aligned16(vq) &&
+                          aligned16(vs) && aligned16(o)))
+    return FATTN_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Skv < 1 || d < 1) return FATTN_EINVAL;
+  if (Hq % Hkv != 0) return FATTN_EINVAL;
+  if (!std::isfinite(scale)) return FATTN_EINVAL;
+  if (num_splits < 0) return FATTN_EINVAL;
+  if (!fits(B, Hkv, Skv, d) || !fits(B, Hq, d, 1)) return FATTN_EINVAL;
+  if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
+  return FATTN_OK;
+}
+
+size_t workspace_bytes_for(int B, int Hq, int nsplit, int d) {
+  // partial outputs [B, Hq, nsplit, d] fp32, then partial lse [B, Hq, nsplit]
+  // fp32, the second array starting on a 256-byte boundary.
+  size_t rows = size_t(B) * size_t(Hq) * size_t(nsplit);
+  size_t o_bytes = (rows * size_t(d) * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + rows * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int Sq, int Skv, int d,
+              float scale, int causal, int window, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return FATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FATTN_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || d < 1) return FATTN_EINVAL;
+  if (Hq % Hkv != 0) return FATTN_EINVAL;
+  if (!std::isfinite(scale)) return FATTN_EINVAL;
+  if (causal != 0 && causal != 1) return FATTN_EINVAL;
+  if (window < 0 || (window > 0 && !causal)) return FATTN_EINVAL;
+  if (!fits(B, Sq, Hq, d) || !fits(B, Skv, Hkv, d)) return FATTN_EINVAL;
+  // the kernels use one-dimensional grids of at most B*Hq*ceil(Sq/4) blocks
+  if (int64_t(B) * Hq * ((int64_t(Sq) + 3) / 4) > 0x7fffffff) return FATTN_EINVAL;
+  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
+  if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
+
+  fattn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, d, scale, causal, window};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dtype == FATTN_F32 ? fattn::launch_fwd_f32(a, s) : fattn::launch_fwd_bf16(a, s);
+  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+}
+
+int fattn_decode_num_splits(int B, int Hq, int Hkv, int Skv, int d, int num_splits) {
+  int st = validate_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           B, Hq, Hkv, Skv, d, 1.0f, num_splits, false);
+  if (st != FATTN_OK) return st;
+  int nsplit, chunk;
+  plan_splits(B, Hkv, Skv, num_splits, &nsplit, &chunk);
+  return nsplit;
+}
+
+size_t fattn_decode_workspace_size(int B, int Hq, int Hkv, int Skv, int d, int num_splits) {
+  int nsplit = fattn_decode_num_splits(B, Hq, Hkv, Skv, d, num_splits);
+  if (nsplit < 1) return 0;
+  return workspace_bytes_for(B, Hq, nsplit, d);
+}
+
+int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_scale,
+                      const int8_t* vq, const float* v_scale, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Skv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int st = validate_decode(q, kq, k_scale, vq, v_scale, o, B, Hq, Hkv, Skv, d, scale,
+                           num_splits, true);
+  if (st != FATTN_OK) return st;
+  int nsplit, chunk;
+  plan_splits(B, Hkv, Skv, num_splits, &nsplit, &chunk);
+  size_t need = workspace_bytes_for(B, Hq, nsplit, d);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FATTN_EWORKSPACE;
+  if (lse && !aligned16(lse)) return FATTN_EINVAL;
+
+  size_t rows = size_t(B) * size_t(Hq) * size_t(nsplit);
+  size_t o_bytes = (rows * size_t(d) * sizeof(float) + 255) / 256 * 256;
+  fattn::DecodeArgs a{q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
+                      nsplit, chunk, static_cast<float*>(workspace),
+                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes)};
+  hipError_t err = fattn::launch_decode_int8(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+}
+
+const char* fattn_status_string(int status) {
+  switch (status) {
+    case FATTN_OK: return "ok";
+    case FATTN_EINVAL: return "invalid argument";
+    case FATTN_EUNSUPPORTED: return "unsupported head_dim or dtype";
+    case FATTN_EWORKSPACE: return "workspace missing or too small";
+    case FATTN_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fattn_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,329 @@
+// bf16 tiled exact attention on the gfx950 matrix cores.
+//
+// Method ([FA-NPU] tiling section; [FA-3MOVES] moves 1 and 2): a block owns a
+// tile of query rows and streams key/value tiles through LDS; per tile it
+// forms the scores with matrix-core products, folds them into a running row
+// max m and row sum l (rescaling the accumulator by 2^(m_old - m_new) when
+// the max grows), and accumulates P.V.  Scores never leave registers.
+//
+// gfx950 design:
+//  * 256 threads = 4 waves; each wave owns 32 query rows, the block 128.
+//    Rows enumerate (position, query head) with the head fastest inside a
+//    chunk of GC heads that share one kv head (GQA/MQA, [FA-VARIANTS] GQA
+//    section): one K/V tile in LDS serves GC heads x 128/GC positions, and no
+//    K/V copy is ever made.
+//  * scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the wave's Q rows
+//    held in registers).  In that output layout each lane holds one query
+//    row and 16 keys, so the probabilities are already the B operand of
+//    O^T += V^T P^T, and the accumulator of each lane is its own query row:
+//    the softmax row statistics need one cross-lane step (lane ^ 32).
+//  * V^T is read from a row-major V tile with ds_read_b64_tr_b16, the
+//    transposing LDS read, in the key order the P layout dictates.
+//  * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global
+//    loads are in flight (registers) while the current one is computed.  LDS
+//    rows are XOR-swizzled in 16-byte chunks to spread banks.
+//  * causal/window: blocks visit only key tiles that intersect their visible
+//    band; waves skip tiles with no visible key for their rows; the mask is
+//    applied only on tiles that straddle a band edge.  Heavy (late) query
+//    blocks are dispatched first.
+//  * softmax in base 2 with the scale folded in: p = 2^(s*c - m), c =
+//    scale*log2(e); a negative scale is applied as an exact sign flip of Q.
+#include "device_util.h"
+#include "launch.h"
+
+#include <cmath>
+
+namespace fattn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per block
+constexpr int kBN = 64;           // keys per tile
+constexpr float kNegHuge = -1e30f;
+constexpr float kLn2 = 0.693147180559945309f;
+
+struct Params {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  int Hq, Hkv, Sq, Skv;
+  int G;         // query heads per kv head
+  int gc_shift;  // log2 of the heads per row chunk (GC)
+  int nchunk;    // G / GC
+  int nqb;       // row blocks per (b, kv head, head chunk)
+  int nx;        // B * Hkv * nchunk
+  float c;       // |scale| * log2(e), >= 1e-30
+  int negate;    // 1 if scale < 0 (Q sign flipped on load)
+  int causal, window;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
+  constexpr int KCH = D / 8;                  // 16-byte chunks per K/V row
+  constexpr int KSTEPS = D / 16;              // k-steps of the QK^T product
+  constexpr int NB = D / 32;                  // 32-wide blocks of the output row
+  constexpr int TILE_CHUNKS = kBN * KCH;      // 16-byte chunks per K (or V) tile
+  constexpr int LOADS = TILE_CHUNKS / kThreads;
+  static_assert(TILE_CHUNKS % kThreads == 0, "tile must split evenly over threads");
+  __shared__ uint4 lds[2][2][TILE_CHUNKS];    // [buffer][K, V][swizzled chunk]
+
+  // ---- block -> (batch, kv head, head chunk, query block); heavy blocks first
+  const int id = blockIdx.x;
+  const int x = id % p.nx;
+  const int slot = id / p.nx;
+  const int qb = p.causal ? p.nqb - 1 - slot : slot;
+  const int chunk = x % p.nchunk;
+  const int hk = (x / p.nchunk) % p.Hkv;
+  const int b = x / (p.nchunk * p.Hkv);
+  const int gc = 1 << p.gc_shift;
+  const int rows_pos = kBM >> p.gc_shift;     // positions per block
+  const int p0 = qb * rows_pos;
+  const int hq0 = hk * p.G + chunk * gc;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int lq = lane & 31;
+  const int hh = lane >> 5;
+  const int row = w * 32 + lq;
+  const int pos = p0 + (row >> p.gc_shift);
+  const int hq = hq0 + (row & (gc - 1));
+  const bool row_ok = pos < p.Sq;
+  const int64_t off = int64_t(p.Skv) - p.Sq;
+
+  // ---- key ranges: block band [jb, je); this row's visible keys [row_lo, row_hi)
+  const int bpos_hi = min(p0 + rows_pos - 1, p.Sq - 1);
+  int64_t jb = 0, je = p.Skv;
+  int64_t row_lo = 0, row_hi = p.Skv;
+  const int wpos_lo = p0 + ((w * 32) >> p.gc_shift);
+  const int wpos_hi = min(p0 + ((w * 32 + 31) >> p.gc_shift), p.Sq - 1);
+  int64_t w_hi_min = p.Skv, w_hi_max = p.Skv, w_lo_min = 0, w_lo_max = 0;
+  if (p.causal) {
+    je = min(int64_t(p.Skv), bpos_hi + off + 1);
+    row_hi = min(int64_t(p.Skv), pos + off + 1);
+    w_hi_min = min(int64_t(p.Skv), wpos_lo + off + 1);
+    w_hi_max = min(int64_t(p.Skv), wpos_hi + off + 1);
+    if (p.window > 0) {
+      jb = max(int64_t(0), p0 + off - p.window + 1);
+      row_lo = max(int64_t(0), pos + off - p.window + 1);
+      w_lo_min = max(int64_t(0), wpos_lo + off - p.window + 1);
+      w_lo_max = max(int64_t(0), wpos_hi + off - p.window + 1);
+    }
+  }
+  const bool wave_active = wpos_lo < p.Sq;
+  const int ntiles = je > jb ? int((je - jb + kBN - 1) / kBN) : 0;
+
+  // ---- Q rows of this wave as the B operand (k-step m: columns 16m + 8hh .. +7)
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16* qrow = p.q + ((int64_t(b) * p.Sq + (row_ok ? pos : 0)) * p.Hq + hq) * D;
+#pragma unroll
+    for (int m = 0; m < KSTEPS; ++m) {
+      uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * m + 8 * hh);
+      if (p.negate) {
+        raw.x ^= 0x80008000u; raw.y ^= 0x80008000u; raw.z ^= 0x80008000u; raw.w ^= 0x80008000u;
+      }
+      qf[m] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+  float m_run = kNegHuge, l_run = 0.f;
+
+  const int64_t kv_stride = int64_t(p.Hkv) * D;
+  const __bf16* kbase = p.k + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
+  const __bf16* vbase = p.v + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
+
+  uint4 kreg[LOADS], vreg[LOADS];
+  auto gload = [&](int64_t j0) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int r = e / KCH, ch = e % KCH;
+      const int64_t j = j0 + r;
+      if (j < je) {
+        kreg[i] = *reinterpret_cast<const uint4*>(kbase + j * kv_stride + ch * 8);
+        vreg[i] = *reinterpret_cast<const uint4*>(vbase + j * kv_stride + ch * 8);
+      } else {
+        kreg[i] = make_uint4(0u, 0u, 0u, 0u);
+        vreg[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int r = e / KCH, ch = e % KCH;
+      const int slotc = r * KCH + (ch ^ (r & (KCH - 1)));
+      lds[buf][0][slotc] = kreg[i];
+      lds[buf][1][slotc] = vreg[i];
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(jb);
+    lstore(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int64_t j0 = jb + int64_t(t) * kBN;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) gload(j0 + kBN);
+
+    const bool visit = wave_active && j0 < w_hi_max && j0 + kBN > w_lo_min;
+    if (visit) {
+      const uint4* Kl = lds[buf][0];
+      const char* Vb = reinterpret_cast<const char*>(lds[buf][1]);
+
+      // S^T = K Q^T for two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const int kr = kb * 32 + lq;
+#pragma unroll
+        for (int m = 0; m < KSTEPS; ++m) {
+          const int ch = 2 * m + hh;
+          const bf16x8 a = __builtin_bit_cast(bf16x8, Kl[kr * KCH + (ch ^ (kr & (KCH - 1)))]);
+          s[kb] = mfma32(a, qf[m], s[kb]);
+        }
+      }
+
+      // mask only where the tile straddles an edge of this wave's band
+      const bool need_mask = (j0 + kBN > w_hi_min) || (j0 < w_lo_max);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key < row_lo || key >= row_hi) s[kb][r] = -INFINITY;
+          }
+        }
+      }
+
+      // online softmax (base 2, scale folded into c)
+      float mx = kNegHuge;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      }
+      mx = wave_max_xor(mx, 32);
+      const float m_new = fmaxf(m_run, mx * p.c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+
+      bf16x8 pf[4];
+      float ls = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -m_new));
+          ls += e[i];
+        }
+        pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      }
+      l_run = l_run * alpha + ls;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+      }
+
+      // O^T += V^T P^T; V^T via transposed LDS reads in the key order of pf
+      const int g16 = lane >> 4, s16 = lane & 15;
+      const int h2 = g16 >> 1, nh = g16 & 1;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const int r0 = kc * 16 + 4 * h2 + (s16 >> 2);
+        const int r1 = r0 + 8;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = nb * 32 + nh * 16 + 4 * (s16 & 3);
+          const int o0 = (r0 * KCH + ((col >> 3) ^ (r0 & (KCH - 1)))) * 16 + (col & 7) * 2;
+          const int o1 = (r1 * KCH + ((col >> 3) ^ (r1 & (KCH - 1)))) * 16 + (col & 7) * 2;
+          const i16x4 a0 = lds_read_tr16(Vb + o0);
+          const i16x4 a1 = lds_read_tr16(Vb + o1);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, concat_i16x4(a0, a1));
+          acc[nb] = mfma32(av, pf[kc], acc[nb]);
+        }
+      }
+    }
+
+    if (t + 1 < ntiles) lstore((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log)
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  __bf16* orow = p.o + ((int64_t(b) * p.Sq + pos) * p.Hq + hq) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 ov;
+      ov[0] = (__bf16)(acc[nb][4 * g + 0] * inv);
+      ov[1] = (__bf16)(acc[nb][4 * g + 1] * inv);
+      ov[2] = (__bf16)(acc[nb][4 * g + 2] * inv);
+      ov[3] = (__bf16)(acc[nb][4 * g + 3] * inv);
+      *reinterpret_cast<bf16x4*>(orow + nb * 32 + 8 * g + 4 * hh) = ov;
+    }
+  }
+  if (hh == 0 && p.lse) {
+    p.lse[(int64_t(b) * p.Hq + hq) * p.Sq + pos] =
+        l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+  }
+}
+
+int heads_per_chunk_shift(int G) {
+  int s = 0;
+  while (s < 5 && (G % (2 << s)) == 0) ++s;  // largest power of two <= 32 dividing G
+  return s;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+  Params p;
+  p.q = static_cast<const __bf16*>(a.q);
+  p.k = static_cast<const __bf16*>(a.k);
+  p.v = static_cast<const __bf16*>(a.v);
+  p.o = static_cast<__bf16*>(a.o);
+  p.lse = a.lse;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.Sq = a.Sq;
+  p.Skv = a.Skv;
+  p.G = a.Hq / a.Hkv;
+  p.gc_shift = heads_per_chunk_shift(p.G);
+  p.nchunk = p.G >> p.gc_shift;
+  const int rows_pos = kBM >> p.gc_shift;
+  p.nqb = (a.Sq + rows_pos - 1) / rows_pos;
+  p.nx = a.B * a.Hkv * p.nchunk;
+  float c = std::fabs(a.scale) * 1.4426950408889634f;
+  p.c = c < 1e-30f ? 1e-30f : c;
+  p.negate = a.scale < 0.f ? 1 : 0;
+  p.causal = a.causal;
+  p.window = a.window;
+  const int64_t blocks = int64_t(p.nqb) * p.nx;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.d == 64) {
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fattn

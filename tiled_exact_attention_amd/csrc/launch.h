@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer (fattn_api.cpp) and the kernel
+// translation units.  Not installed; the public interface is include/fattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fattn {
+
+// Arguments of one prefill call after validation.  Pointers are device
+// pointers; q/o are [B, Sq, Hq, d], k/v [B, Skv, Hkv, d], lse [B, Hq, Sq] or null.
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Skv, d;
+  float scale;
+  int causal;
+  int window;
+};
+
+// Arguments of one int8-cache decode call after validation and split planning.
+struct DecodeArgs {
+  const void* q;          // [B, Hq, d] bf16
+  const int8_t* kq;       // [B, Hkv, Skv, d]
+  const float* kscale;    // [B, Hkv, Skv]
+  const int8_t* vq;
+  const float* vscale;
+  void* o;                // [B, Hq, d] bf16
+  float* lse;             // [B, Hq] or null
+  int B, Hq, Hkv, Skv, d;
+  float scale;
+  int nsplit;             // key splits per (b, kv head)
+  int chunk;              // tokens per split (a multiple of the kernel's key tile)
+  float* part_o;          // workspace: [B, Hq, nsplit, d] fp32
+  float* part_lse;        // workspace: [B, Hq, nsplit] fp32
+};
+
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream);
+
+// Key-tile length of the decode split kernel; split chunks are multiples of it.
+constexpr int kDecodeTile = 64;
+
+}  // namespace fattn
