@@ -1,0 +1,292 @@
+"""Benchmark of the tiled exact attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * fattn_fwd on the MHA causal prefill workload (B=2, H=32, S=4096, d=128,
+    bf16), the workload the headline metric is quoted on, and
+  * fattn_decode_int8 on the GQA int8-KV-cache decode workload (B=32, Hq=32,
+    Hkv=8, Skv=32768, d=128).
+Inputs are resident in HBM before timing starts.  `value` is the prefill
+attention throughput in TFLOP/s (4*d FLOPs per visible (query, key) pair per
+query head, counted exactly); the decode leg reports HBM GB/s over its
+algorithmic bytes (int8 K and V, their fp32 scales, the bf16 query and output).
+Each kernel call is timed with HIP events recorded on the stream it runs on
+(torch's current stream, which the binding passes to libfattn).
+
+The CPU baseline times the fp64 oracle on the host on a bounded sample of the
+prefill workload (whole query rows of a few (batch, head) pairs).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s & % bf16 MFMA peak (prefill); HBM GB/s & % peak (decode)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
+PREFILL_KERNEL_SRC = os.path.join(ROOT, "tiled_exact_attention_amd", "csrc", "fwd_bf16.hip")
+DECODE_KERNEL_SRC = os.path.join(ROOT, "tiled_exact_attention_amd", "csrc", "decode_int8.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def visible_pairs(Sq, Skv, causal, window):
+    """Number of visible (query, key) pairs of one head (exact count)."""
+    off = Skv - Sq
+    if not causal:
+        return Sq * Skv
+    total = 0
+    for i in range(Sq):
+        hi = min(Skv, i + off + 1)
+        lo = max(0, i + off - window + 1) if window else 0
+        total += max(0, hi - lo)
+    return total
+
+
+def prefill_flops(w):
+    return 4 * w.d * visible_pairs(w.Sq, w.Skv, w.causal, w.window) * w.B * w.Hq
+
+
+def decode_bytes(w):
+    kv = 2 * w.B * w.Hkv * w.Skv * w.d          # int8 codes of K and V
+    scales = 2 * w.B * w.Hkv * w.Skv * 4         # fp32 scales
+    qo = 2 * w.B * w.Hq * w.d * 2                # bf16 query and output
+    return kv + scales + qo
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel_src, key):
+    """HBM bytes per launch measured with rocprofv3 counters, if they are current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get(f"{key}_source_sha256") != source_hash(kernel_src):
+        return None  # the kernel changed since the counters were taken
+    try:
+        return float(vals[f"{key}_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_cpu_baseline(w, q, k, v, budget_s):
+    """Times the fp64 oracle on whole query rows of (b, h) pairs, growing the
+    sample until about budget_s seconds of CPU work have been measured."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.max_threads(0)
+    qd = q.double().numpy()
+    kd = k.double().numpy()
+    vd = v.double().numpy()
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(pairs)
+    done_flops, elapsed, used = 0, 0.0, 0
+    per_head = 4 * w.d * visible_pairs(w.Sq, w.Skv, w.causal, w.window)
+    while used < len(pairs) and elapsed < budget_s:
+        n = 1 if used == 0 else max(1, min(len(pairs) - used,
+                                           int((budget_s - elapsed) / max(elapsed / used, 1e-9))))
+        chunk = pairs[used:used + n]
+        rows = np.array([(b, h, i) for b, h in chunk for i in range(w.Sq)], dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.fwd(qd, kd, vd, causal=w.causal, window=w.window, scale=w.scale, rows=rows,
+                   threads=threads)
+        elapsed += time.perf_counter() - t0
+        done_flops += per_head * len(chunk)
+        used += len(chunk)
+    return {
+        "value": round(done_flops / elapsed / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{used} of {len(pairs)} (batch, head) pairs of the {w.name} workload, every "
+                  f"query row, fp64 three-pass oracle; {done_flops / 1e9:.1f} GFLOP in {elapsed:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+                    help="time one leg only (for profiler runs); the JSON line is then partial")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--num-splits", type=int, default=0, help="decode key splits (0 = library default)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_exact_attention_amd as fa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    wp, wd = W.MHA_CAUSAL, W.INT8_DECODE
+    do_prefill = args.only in ("all", "prefill")
+    do_decode = args.only in ("all", "decode")
+
+    if do_prefill:
+        log(f"generating {wp.name}")
+        q_cpu, k_cpu, v_cpu = W.workload_inputs(wp)
+        q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((wp.B, wp.Hq, wp.Sq), dtype=torch.float32, device=dev)
+    if do_decode:
+        log(f"generating {wd.name}")
+        dq, dkq, dks, dvq, dvs = W.decode_workload_inputs(wd, device=dev)
+        d_o = torch.empty_like(dq)
+        d_lse = torch.empty((wd.B, wd.Hq), dtype=torch.float32, device=dev)
+        ws = torch.empty((fa.decode_workspace_size(wd.B, wd.Hq, wd.Hkv, wd.Skv, wd.d, args.num_splits),),
+                         dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def run_prefill():
+        st = fa.fattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          wp.B, wp.Hq, wp.Hkv, wp.Sq, wp.Skv, wp.d, wp.scale, int(wp.causal),
+                          wp.window, fa.FATTN_BF16, stream.cuda_stream)
+        if st != 0:
+            raise fa.FattnError(st, "fattn_fwd")
+
+    def run_decode():
+        st = fa.fattn_decode_int8(dq.data_ptr(), dkq.data_ptr(), dks.data_ptr(), dvq.data_ptr(),
+                                  dvs.data_ptr(), d_o.data_ptr(), d_lse.data_ptr(), wd.B, wd.Hq,
+                                  wd.Hkv, wd.Skv, wd.d, wd.scale, args.num_splits, ws.data_ptr(),
+                                  ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise fa.FattnError(st, "fattn_decode_int8")
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        if do_prefill:
+            run_prefill()
+        if do_decode:
+            run_decode()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        if do_prefill:
+            run_prefill()
+        ev[s][1].record(stream)
+        if do_decode:
+            run_decode()
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(args.steps)]
+    dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    log(f"prefill avg {pre_avg * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us, wall {wall * 1e3 / args.steps:.3f} ms/step")
+
+    result = {
+        "metric": METRIC,
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wp.name} + {wd.name}", "prefill": {
+            "B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "S": wp.Sq, "d": wp.d, "causal": wp.causal,
+            "layout": "BSHD", "seed": wp.seed}, "decode": {
+            "B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "Skv": wd.Skv, "d": wd.d, "kv": "int8 + fp32 scale per token/head",
+            "num_splits": fa.decode_num_splits(wd.B, wd.Hq, wd.Hkv, wd.Skv, wd.d, args.num_splits),
+            "seed": wd.seed}},
+    }
+    if do_prefill:
+        flops = prefill_flops(wp)
+        tflops = flops / (pre_avg * 1e-3) / 1e12
+        traffic = read_traffic(PREFILL_KERNEL_SRC, "prefill")
+        result["value"] = round(tflops, 2)
+        result["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                              "traffic": traffic, "kernel": "fwd_bf16_kernel<128>",
+                              "algorithmic_flop_per_launch": flops,
+                              "avg_launch_us": round(pre_avg * 1e3, 2)}
+    if do_decode:
+        nbytes = decode_bytes(wd)
+        gbs = nbytes / (dec_avg * 1e-3) / 1e9
+        result["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "avg_call_us": round(dec_avg * 1e3, 2),
+                            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                         "traffic": read_traffic(DECODE_KERNEL_SRC, "decode"),
+                                         "kernel": "decode_split_kernel<128> + decode_merge_kernel<128>",
+                                         "algorithmic_bytes_per_call": nbytes}}
+        if not do_prefill:
+            result["value"], result["unit"] = round(gbs, 1), "GB/s"
+
+    if do_prefill and args.only == "all":
+        # the other prefill workloads, informational (same kernel, same timing method)
+        others = {}
+        for w in (W.GQA_CAUSAL, W.MQA_CAUSAL, W.MQA_WINDOW):
+            qq, kk, vv = (t.to(dev) for t in W.workload_inputs(w))
+            oo = torch.empty_like(qq)
+            for _ in range(3):
+                fa.fwd(qq, kk, vv, causal=w.causal, window=w.window, scale=w.scale, out=oo)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            e0.record(stream)
+            for _ in range(reps):
+                fa.fwd(qq, kk, vv, causal=w.causal, window=w.window, scale=w.scale, out=oo)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            tf = prefill_flops(w) / (us * 1e-6) / 1e12
+            others[w.name] = {"us": round(us, 2), "TFLOP/s": round(tf, 2),
+                              "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del qq, kk, vv, oo
+        result["prefill_other_workloads"] = others
+
+    if do_prefill and not args.no_cpu_baseline:
+        log(f"cpu baseline: fp64 oracle, about {args.cpu_budget:.0f} s")
+        result["cpu_baseline"] = time_cpu_baseline(wp, q_cpu, k_cpu, v_cpu, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
