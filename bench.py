@@ -131,8 +131,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
-                    help="time one leg only (for profiler runs); the JSON line is then partial")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "copy"), default="all",
+                    help="time one leg only (for profiler runs); the JSON line is then partial. "
+                         "'copy' times a plain 1 GiB device-to-device copy, the known-size "
+                         "reference that scales the HBM byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--num-splits", type=int, default=0, help="decode key splits (0 = library default)")
@@ -154,6 +156,24 @@ def main():
     fa.load()
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / max(args.steps, 1)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "avg_us": round(us, 2),
+                          "GB/s": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
+        return
 
     wp, wd = W.MHA_CAUSAL, W.INT8_DECODE
     do_prefill = args.only in ("all", "prefill")

@@ -42,6 +42,29 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Asynchronous 16-byte-per-lane copy HBM -> LDS (global_load_lds_dwordx4):
+// lane l's 16 bytes from gsrc land at lds_dst + 16*l; lds_dst must be the same
+// for every lane of the wave.  Completion is tracked by vmcnt (wait_vmcnt).
+__device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(
+      (const __attribute__((address_space(1))) void*)(gsrc),
+      (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
+}
+
+// Asynchronous 4-byte-per-lane copy HBM -> LDS (global_load_lds_dword).
+__device__ __forceinline__ void global_to_lds4(const void* gsrc, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(
+      (const __attribute__((address_space(1))) void*)(gsrc),
+      (__attribute__((address_space(3))) void*)(lds_dst), 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Transposed 16-bit LDS read (see the layout note above); p is an LDS address.
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(FATTN_LDS(i16x4, const_cast<void*>(p)));

@@ -20,9 +20,11 @@
 //    the softmax row statistics need one cross-lane step (lane ^ 32).
 //  * V^T is read from a row-major V tile with ds_read_b64_tr_b16, the
 //    transposing LDS read, in the key order the P layout dictates.
-//  * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global
-//    loads are in flight (registers) while the current one is computed.  LDS
-//    rows are XOR-swizzled in 16-byte chunks to spread banks.
+//  * K/V tiles of 64 keys are double-buffered in LDS and filled straight
+//    from HBM by global_load_lds_dwordx4 (no register staging): the next
+//    tile streams in while the current one is computed.  LDS rows are
+//    XOR-swizzled in 16-byte chunks to spread banks; each lane's LDS read
+//    offsets are computed once, the stage and block offsets are immediates.
 //  * causal/window: blocks visit only key tiles that intersect their visible
 //    band; waves skip tiles with no visible key for their rows; the mask is
 //    applied only on tiles that straddle a band edge.  Heavy (late) query
@@ -62,14 +64,18 @@ struct Params {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
-  constexpr int KCH = D / 8;                  // 16-byte chunks per K/V row
-  constexpr int KSTEPS = D / 16;              // k-steps of the QK^T product
-  constexpr int NB = D / 32;                  // 32-wide blocks of the output row
-  constexpr int TILE_CHUNKS = kBN * KCH;      // 16-byte chunks per K (or V) tile
-  constexpr int LOADS = TILE_CHUNKS / kThreads;
-  static_assert(TILE_CHUNKS % kThreads == 0, "tile must split evenly over threads");
-  __shared__ uint4 lds[2][2][TILE_CHUNKS];    // [buffer][K, V][swizzled chunk]
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
+  constexpr int KCH = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int ROWB = D * 2;                // bytes per K/V row
+  constexpr int TILE_B = kBN * ROWB;         // bytes of one K (or V) tile
+  constexpr int STAGE_B = 2 * TILE_B;        // K tile then V tile
+  constexpr int LPI = 1024 / ROWB;           // rows filled by one 1 KB LDS-DMA instruction
+  constexpr int NLD = kBN / (kWaves * LPI);  // LDS-DMA instructions per wave per tensor per tile
+  constexpr int KSTEPS = D / 16;             // k-steps of the QK^T product
+  constexpr int NB = D / 32;                 // 32-wide blocks of the output row
+  static_assert(NLD * LPI * kWaves == kBN, "tile rows must split evenly over the waves");
+  static_assert(STAGE_B + TILE_B + (kBN / 2) * ROWB <= 65536 + STAGE_B, "offsets fit");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_B];
 
   // ---- block -> (batch, kv head, head chunk, query block); heavy blocks first
   const int id = blockIdx.x;
@@ -130,137 +136,137 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(Params p) {
     }
   }
 
+  // ---- LDS layout: row r of a tile at r*ROWB, its 16-byte chunk c stored at
+  // position c ^ (r % KCH).  Per-lane byte offsets, fixed for the whole kernel:
+  //  K reads (A operand of S^T = K Q^T): row lq (+32 for the second key block),
+  //  chunk 2m + hh;  V reads (transposed, A operand of O^T = V^T P^T): rows
+  //  16kc + 4*h2 + (s16 >> 2) + 8R, columns nb*32 + 16*nh + 4*(s16 & 3).
+  int koff[KSTEPS];
+#pragma unroll
+  for (int m = 0; m < KSTEPS; ++m) koff[m] = lq * ROWB + (((2 * m + hh) ^ (lq & (KCH - 1))) << 4);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int h2 = g16 >> 1, nh = g16 & 1;
+  int voff[NB][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int R = 0; R < 2; ++R) {
+      const int r = 4 * h2 + (s16 >> 2) + 8 * R;
+      const int col = nb * 32 + nh * 16 + 4 * (s16 & 3);
+      voff[nb][R] = TILE_B + r * ROWB + (((col >> 3) ^ (r & (KCH - 1))) << 4) + (col & 7) * 2;
+    }
+  }
+
+  // ---- LDS-DMA load assignment: wave w fills rows 16w .. 16w+15 of a tile;
+  // instruction i covers rows 16w + LPI*i + (lane / KCH), lane's physical
+  // chunk lane % KCH holds logical chunk (lane % KCH) ^ (row % KCH).
+  const int64_t kv_stride = int64_t(p.Hkv) * D;
+  const __bf16* kbase = p.k + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
+  const __bf16* vbase = p.v + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
+  int ld_row[NLD], ld_col[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int r = 16 * w + LPI * i + lane / KCH;
+    ld_row[i] = r;
+    ld_col[i] = ((lane % KCH) ^ (r & (KCH - 1))) * 8;
+  }
+  auto issue_loads = [&](int64_t j0, char* stage) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int64_t j = min(j0 + ld_row[i], int64_t(p.Skv) - 1);  // rows past the end: any valid row
+      const int64_t e = j * kv_stride + ld_col[i];
+      char* dst = stage + (16 * w + LPI * i) * ROWB;
+      global_to_lds16(kbase + e, dst);
+      global_to_lds16(vbase + e, dst + TILE_B);
+    }
+  };
+
   f32x16 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
   float m_run = kNegHuge, l_run = 0.f;
 
-  const int64_t kv_stride = int64_t(p.Hkv) * D;
-  const __bf16* kbase = p.k + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
-  const __bf16* vbase = p.v + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
-
-  uint4 kreg[LOADS], vreg[LOADS];
-  auto gload = [&](int64_t j0) {
+  auto compute = [&](int64_t j0, const char* stage) {
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 s[2];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int r = e / KCH, ch = e % KCH;
-      const int64_t j = j0 + r;
-      if (j < je) {
-        kreg[i] = *reinterpret_cast<const uint4*>(kbase + j * kv_stride + ch * 8);
-        vreg[i] = *reinterpret_cast<const uint4*>(vbase + j * kv_stride + ch * 8);
-      } else {
-        kreg[i] = make_uint4(0u, 0u, 0u, 0u);
-        vreg[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + koff[m] + kb * 32 * ROWB);
+        s[kb] = mfma32(a, qf[m], s[kb]);
+      }
+    }
+
+    // mask only where the tile straddles an edge of this wave's band
+    const bool need_mask = (j0 + kBN > w_hi_min) || (j0 < w_lo_max);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key < row_lo || key >= row_hi) s[kb][r] = -INFINITY;
+        }
+      }
+    }
+
+    // online softmax (base 2, scale folded into c)
+    float mx = kNegHuge;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    }
+    mx = wave_max_xor(mx, 32);
+    const float m_new = fmaxf(m_run, mx * p.c);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+
+    bf16x8 pf[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -m_new));
+        ls += e[i];
+      }
+      pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    }
+    l_run = l_run * alpha + ls;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+    }
+
+    // O^T += V^T P^T; V^T via transposed LDS reads in the key order of pf
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const i16x4 a0 = lds_read_tr16(stage + voff[nb][0] + kc * 16 * ROWB);
+        const i16x4 a1 = lds_read_tr16(stage + voff[nb][1] + kc * 16 * ROWB);
+        acc[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(a0, a1)), pf[kc], acc[nb]);
       }
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int r = e / KCH, ch = e % KCH;
-      const int slotc = r * KCH + (ch ^ (r & (KCH - 1)));
-      lds[buf][0][slotc] = kreg[i];
-      lds[buf][1][slotc] = vreg[i];
-    }
-  };
 
-  if (ntiles > 0) {
-    gload(jb);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
+  // ---- main loop: tile t lives in stage t % 2; tile t+1 streams into the
+  // other stage (HBM -> LDS, no registers) while tile t is computed.
+  auto step = [&](int t, char* cur, char* nxt) {
+    wait_vmcnt<0>();   // this wave's copies of tile t have landed
+    __syncthreads();   // ... and everyone's; everyone is also done with tile t-1
+    if (t + 1 < ntiles) issue_loads(jb + int64_t(t + 1) * kBN, nxt);
     const int64_t j0 = jb + int64_t(t) * kBN;
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(j0 + kBN);
-
-    const bool visit = wave_active && j0 < w_hi_max && j0 + kBN > w_lo_min;
-    if (visit) {
-      const uint4* Kl = lds[buf][0];
-      const char* Vb = reinterpret_cast<const char*>(lds[buf][1]);
-
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int kr = kb * 32 + lq;
-#pragma unroll
-        for (int m = 0; m < KSTEPS; ++m) {
-          const int ch = 2 * m + hh;
-          const bf16x8 a = __builtin_bit_cast(bf16x8, Kl[kr * KCH + (ch ^ (kr & (KCH - 1)))]);
-          s[kb] = mfma32(a, qf[m], s[kb]);
-        }
-      }
-
-      // mask only where the tile straddles an edge of this wave's band
-      const bool need_mask = (j0 + kBN > w_hi_min) || (j0 < w_lo_max);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key < row_lo || key >= row_hi) s[kb][r] = -INFINITY;
-          }
-        }
-      }
-
-      // online softmax (base 2, scale folded into c)
-      float mx = kNegHuge;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      }
-      mx = wave_max_xor(mx, 32);
-      const float m_new = fmaxf(m_run, mx * p.c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-
-      bf16x8 pf[4];
-      float ls = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -m_new));
-          ls += e[i];
-        }
-        pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      }
-      l_run = l_run * alpha + ls;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-      }
-
-      // O^T += V^T P^T; V^T via transposed LDS reads in the key order of pf
-      const int g16 = lane >> 4, s16 = lane & 15;
-      const int h2 = g16 >> 1, nh = g16 & 1;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const int r0 = kc * 16 + 4 * h2 + (s16 >> 2);
-        const int r1 = r0 + 8;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int col = nb * 32 + nh * 16 + 4 * (s16 & 3);
-          const int o0 = (r0 * KCH + ((col >> 3) ^ (r0 & (KCH - 1)))) * 16 + (col & 7) * 2;
-          const int o1 = (r1 * KCH + ((col >> 3) ^ (r1 & (KCH - 1)))) * 16 + (col & 7) * 2;
-          const i16x4 a0 = lds_read_tr16(Vb + o0);
-          const i16x4 a1 = lds_read_tr16(Vb + o1);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, concat_i16x4(a0, a1));
-          acc[nb] = mfma32(av, pf[kc], acc[nb]);
-        }
-      }
-    }
-
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
-    __syncthreads();
+    if (wave_active && j0 < w_hi_max && j0 + kBN > w_lo_min) compute(j0, cur);
+  };
+  if (ntiles > 0) issue_loads(jb, lds);
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, lds, lds + STAGE_B);
+    if (t + 1 < ntiles) step(t + 1, lds + STAGE_B, lds);
   }
 
   // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log)
