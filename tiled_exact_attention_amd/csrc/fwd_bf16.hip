@@ -23,7 +23,8 @@
 //  * K/V tiles of 64 keys are double-buffered in LDS and filled straight
 //    from HBM by global_load_lds_dwordx4 (no register staging): the next
 //    tile streams in while the current one is computed.  LDS rows are
-//    XOR-swizzled in 16-byte chunks to spread banks; each lane's LDS read
+//    XOR-swizzled in 16-byte chunks so neither read pattern has bank
+//    conflicts; each lane's LDS read
 //    offsets are computed once, the stage and block offsets are immediates.
 //  * causal/window: blocks visit only key tiles that intersect their visible
 //    band; waves skip tiles with no visible key for their rows; the mask is
@@ -35,6 +36,7 @@
 #include "launch.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace fattn {
 namespace {
@@ -45,6 +47,24 @@ constexpr int kBM = 32 * kWaves;  // query rows per block
 constexpr int kBN = 64;           // keys per tile
 constexpr float kNegHuge = -1e30f;
 constexpr float kLn2 = 0.693147180559945309f;
+// The accumulator and row sum are kept relative to a reference max m_ref
+// (base-2 units) that is only raised when a row's running max exceeds it by
+// more than kLazy; probabilities are then at most 2^kLazy.  Numerator and
+// denominator share m_ref, so the result is the same softmax.
+constexpr float kLazy = 8.f;
+
+// LDS swizzle: chunk c of tile row r is stored at chunk position c ^ swz(r).
+// swz is GF(2)-linear in the low four row bits and chosen so that both read
+// patterns below are free of bank conflicts (16 rows at one chunk for the K
+// reads; 4 consecutive rows x 4 chunks for the transposed V reads).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+  } else {
+    return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+  }
+}
 
 struct Params {
   const __bf16* q;
@@ -91,7 +111,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int hq0 = hk * p.G + chunk * gc;
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (scalar)
   const int lq = lane & 31;
   const int hh = lane >> 5;
   const int row = w * 32 + lq;
@@ -106,17 +126,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   int64_t row_lo = 0, row_hi = p.Skv;
   const int wpos_lo = p0 + ((w * 32) >> p.gc_shift);
   const int wpos_hi = min(p0 + ((w * 32 + 31) >> p.gc_shift), p.Sq - 1);
-  int64_t w_hi_min = p.Skv, w_hi_max = p.Skv, w_lo_min = 0, w_lo_max = 0;
+  int64_t w_hi_max = p.Skv, w_lo_min = 0;
   if (p.causal) {
     je = min(int64_t(p.Skv), bpos_hi + off + 1);
     row_hi = min(int64_t(p.Skv), pos + off + 1);
-    w_hi_min = min(int64_t(p.Skv), wpos_lo + off + 1);
     w_hi_max = min(int64_t(p.Skv), wpos_hi + off + 1);
     if (p.window > 0) {
       jb = max(int64_t(0), p0 + off - p.window + 1);
       row_lo = max(int64_t(0), pos + off - p.window + 1);
       w_lo_min = max(int64_t(0), wpos_lo + off - p.window + 1);
-      w_lo_max = max(int64_t(0), wpos_hi + off - p.window + 1);
     }
   }
   const bool wave_active = wpos_lo < p.Sq;
@@ -137,13 +155,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   }
 
   // ---- LDS layout: row r of a tile at r*ROWB, its 16-byte chunk c stored at
-  // position c ^ (r % KCH).  Per-lane byte offsets, fixed for the whole kernel:
+  // position c ^ swz(r).  Per-lane byte offsets, fixed for the whole kernel:
   //  K reads (A operand of S^T = K Q^T): row lq (+32 for the second key block),
   //  chunk 2m + hh;  V reads (transposed, A operand of O^T = V^T P^T): rows
   //  16kc + 4*h2 + (s16 >> 2) + 8R, columns nb*32 + 16*nh + 4*(s16 & 3).
   int koff[KSTEPS];
 #pragma unroll
-  for (int m = 0; m < KSTEPS; ++m) koff[m] = lq * ROWB + (((2 * m + hh) ^ (lq & (KCH - 1))) << 4);
+  for (int m = 0; m < KSTEPS; ++m) koff[m] = lq * ROWB + (((2 * m + hh) ^ swz<D>(lq)) << 4);
   const int g16 = lane >> 4, s16 = lane & 15;
   const int h2 = g16 >> 1, nh = g16 & 1;
   int voff[NB][2];
@@ -153,31 +171,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     for (int R = 0; R < 2; ++R) {
       const int r = 4 * h2 + (s16 >> 2) + 8 * R;
       const int col = nb * 32 + nh * 16 + 4 * (s16 & 3);
-      voff[nb][R] = TILE_B + r * ROWB + (((col >> 3) ^ (r & (KCH - 1))) << 4) + (col & 7) * 2;
+      voff[nb][R] = TILE_B + r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
     }
   }
 
   // ---- LDS-DMA load assignment: wave w fills rows 16w .. 16w+15 of a tile;
   // instruction i covers rows 16w + LPI*i + (lane / KCH), lane's physical
-  // chunk lane % KCH holds logical chunk (lane % KCH) ^ (row % KCH).
+  // chunk lane % KCH holds logical chunk (lane % KCH) ^ swz(row).
   const int64_t kv_stride = int64_t(p.Hkv) * D;
   const __bf16* kbase = p.k + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
   const __bf16* vbase = p.v + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
-  int ld_row[NLD], ld_col[NLD];
+  int64_t goff[NLD];   // element offset of this lane's source chunk within a tile
+  int ld_row[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int r = 16 * w + LPI * i + lane / KCH;
     ld_row[i] = r;
-    ld_col[i] = ((lane % KCH) ^ (r & (KCH - 1))) * 8;
+    goff[i] = int64_t(r) * kv_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
   }
-  auto issue_loads = [&](int64_t j0, char* stage) {
+  auto issue_loads = [&](int64_t j0, char* stage) __attribute__((always_inline)) {
+    if (j0 + kBN <= p.Skv) {
+      const __bf16* kt = kbase + j0 * kv_stride;
+      const __bf16* vt = vbase + j0 * kv_stride;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int64_t j = min(j0 + ld_row[i], int64_t(p.Skv) - 1);  // rows past the end: any valid row
-      const int64_t e = j * kv_stride + ld_col[i];
-      char* dst = stage + (16 * w + LPI * i) * ROWB;
-      global_to_lds16(kbase + e, dst);
-      global_to_lds16(vbase + e, dst + TILE_B);
+      for (int i = 0; i < NLD; ++i) {
+        char* dst = stage + (16 * w + LPI * i) * ROWB;
+        global_to_lds16(kt + goff[i], dst);
+        global_to_lds16(vt + goff[i], dst + TILE_B);
+      }
+    } else {
+      // last tile of the sequence: rows past the end re-read the last row
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int64_t j = min(j0 + ld_row[i], int64_t(p.Skv) - 1);
+        const int64_t e = goff[i] + (j - ld_row[i]) * kv_stride;
+        char* dst = stage + (16 * w + LPI * i) * ROWB;
+        global_to_lds16(kbase + e, dst);
+        global_to_lds16(vbase + e, dst + TILE_B);
+      }
     }
   };
 
@@ -186,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
   float m_run = kNegHuge, l_run = 0.f;
 
-  auto compute = [&](int64_t j0, const char* stage) {
+  auto compute = [&](int64_t j0, const char* stage, auto masked) __attribute__((always_inline)) {
     // S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
 #pragma unroll
@@ -199,15 +230,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       }
     }
 
-    // mask only where the tile straddles an edge of this wave's band
-    const bool need_mask = (j0 + kBN > w_hi_min) || (j0 < w_lo_max);
-    if (need_mask) {
+    // mask (only on tiles that straddle an edge of this wave's band): key
+    // j0 + kofs is visible iff row_lo <= key < row_hi; kofs - 4*hh is a
+    // compile-time constant per register, so compare against shifted bounds.
+    if constexpr (decltype(masked)::value) {
+      const int lo = int(max(min(row_lo - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
+      const int hi = int(max(min(row_hi - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t key = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key < row_lo || key >= row_hi) s[kb][r] = -INFINITY;
+          const int kc0 = kb * 32 + 8 * (r >> 2) + (r & 3);
+          if (kc0 < lo || kc0 >= hi) s[kb][r] = -INFINITY;
         }
       }
     }
@@ -219,27 +253,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     }
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx * p.c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = max_across_halves(mx) * p.c;
+    if (__builtin_expect(__any(mx > m_run + kLazy), 0)) {  // rare: raise the reference
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
+    }
 
     bf16x8 pf[4];
-    float ls = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       float e[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -m_new));
-        ls += e[i];
+        e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -m_run));
+        l_run += e[i];
       }
       pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-    }
-    l_run = l_run * alpha + ls;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
     }
 
     // O^T += V^T P^T; V^T via transposed LDS reads in the key order of pf
@@ -256,18 +289,39 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 
   // ---- main loop: tile t lives in stage t % 2; tile t+1 streams into the
   // other stage (HBM -> LDS, no registers) while tile t is computed.
-  auto step = [&](int t, char* cur, char* nxt) {
+  // Tiles [t_lo, t_hi) are fully visible to every row of the block and use
+  // the unmasked path; tiles before (window edge) and after (causal edge, end
+  // of the keys) use the masked path, where waves also skip tiles they cannot
+  // see.  Both bounds are even so each stage offset is a compile-time constant.
+  auto step = [&](int t, char* cur, char* nxt, auto masked) __attribute__((always_inline)) {
     wait_vmcnt<0>();   // this wave's copies of tile t have landed
     __syncthreads();   // ... and everyone's; everyone is also done with tile t-1
     if (t + 1 < ntiles) issue_loads(jb + int64_t(t + 1) * kBN, nxt);
     const int64_t j0 = jb + int64_t(t) * kBN;
-    if (wave_active && j0 < w_hi_max && j0 + kBN > w_lo_min) compute(j0, cur);
+    if constexpr (decltype(masked)::value) {
+      if (wave_active && j0 < w_hi_max && j0 + kBN > w_lo_min) compute(j0, cur, masked);
+    } else {
+      if (wave_active) compute(j0, cur, masked);
+    }
   };
-  if (ntiles > 0) issue_loads(jb, lds);
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, lds, lds + STAGE_B);
-    if (t + 1 < ntiles) step(t + 1, lds + STAGE_B, lds);
+  auto pair = [&](int t, auto masked) __attribute__((always_inline)) {
+    step(t, lds, lds + STAGE_B, masked);
+    if (t + 1 < ntiles) step(t + 1, lds + STAGE_B, lds, masked);
+  };
+  int t_lo = 0, t_hi = ntiles;
+  {
+    const int64_t hi_min = p.causal ? min(int64_t(p.Skv), p0 + off + 1) : int64_t(p.Skv);
+    const int64_t lo_max = (p.causal && p.window > 0) ? max(int64_t(0), bpos_hi + off - p.window + 1) : 0;
+    t_hi = hi_min - jb >= kBN ? int(min(int64_t(ntiles), (hi_min - jb) / kBN)) : 0;
+    t_lo = lo_max > jb ? int(min(int64_t(t_hi), (lo_max - jb + kBN - 1) / kBN)) : 0;
+    t_lo = (t_lo + 1) & ~1;
+    t_hi = t_hi > t_lo ? t_lo + ((t_hi - t_lo) & ~1) : t_lo;
   }
+  if (ntiles > 0) issue_loads(jb, lds);
+  int t = 0;
+  for (; t < t_lo; t += 2) pair(t, std::true_type{});
+  for (; t < t_hi; t += 2) pair(t, std::false_type{});
+  for (; t < ntiles; t += 2) pair(t, std::true_type{});
 
   // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
