@@ -2,7 +2,7 @@
 //
 // Validation runs before any HIP call, so an invalid call enqueues nothing and
 // writes nothing, and this part is testable on a machine without a GPU.
-#include "../../include/fattn.h"
+#include "fattn.h"
 #include "launch.h"
 
 #include <cmath>

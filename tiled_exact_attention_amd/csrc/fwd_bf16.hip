@@ -218,7 +218,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   float m_run = kNegHuge, l_run = 0.f;
 
   auto compute = [&](int64_t j0, const char* stage, auto masked) __attribute__((always_inline)) {
-    // S^T = K Q^T for two 32-key blocks
+    // S^T = K Q^T for two 32-key blocks.  Matrix-product runs are issued at
+    // raised wave priority so that, of the two waves sharing a SIMD, the one
+    // streaming products keeps the matrix pipe fed while the other one's
+    // softmax fills the vector ALU.
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -230,6 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // mask (only on tiles that straddle an edge of this wave's band): key
     // j0 + kofs is visible iff row_lo <= key < row_hi; kofs - 4*hh is a
     // compile-time constant per register, so compare against shifted bounds.
@@ -276,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     }
 
     // O^T += V^T P^T; V^T via transposed LDS reads in the key order of pf
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
@@ -285,6 +291,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         acc[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(a0, a1)), pf[kc], acc[nb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- main loop: tile t lives in stage t % 2; tile t+1 streams into the
