@@ -72,10 +72,12 @@ def test_version_and_status_strings():
     assert fa.fattn_status_string(12345) == "unknown status"
 
 
-def _plan(Skv, req, B=1, Hkv=1):
-    """Split plan the header documents: chunks of whole 64-token tiles, no empty split."""
+def _plan(Skv, req, B=1, Hkv=1, Hq=1):
+    """Split plan the header documents: chunks of whole 64-token tiles, no empty split;
+    automatic = as many splits as keep one round of 2048 resident waves."""
     if req == 0:
-        req = min(max(-(-8192 // (B * Hkv)), 1), -(-Skv // 256), 1024)
+        waves_per_split = B * Hkv * (-(-(Hq // Hkv) // 16))
+        req = min(max(2048 // waves_per_split, 1), -(-Skv // 256), 1024)
     req = min(req, Skv)
     chunk = -(-Skv // req)
     chunk = -(-chunk // 64) * 64
@@ -84,10 +86,13 @@ def _plan(Skv, req, B=1, Hkv=1):
 
 @pytest.mark.parametrize("B,Hq,Hkv,Skv,d,req", [
     (32, 32, 8, 32768, 128, 0), (1, 4, 1, 1, 64, 0), (2, 8, 2, 1000, 128, 7),
-    (1, 1, 1, 65, 64, 3), (3, 6, 3, 4097, 128, 16), (1, 2, 2, 64, 64, 64), (4, 4, 4, 70000, 64, 0)])
+    (1, 1, 1, 65, 64, 3), (3, 6, 3, 4097, 128, 16), (1, 2, 2, 64, 64, 64), (4, 4, 4, 70000, 64, 0),
+    (1, 40, 2, 100000, 128, 0), (300, 8, 1, 4096, 64, 0)])
 def test_split_plan_and_workspace_size(B, Hq, Hkv, Skv, d, req):
     n = fa.decode_num_splits(B, Hq, Hkv, Skv, d, req)
-    want_n, chunk = _plan(Skv, req, B, Hkv)
+    if req == 0:  # automatic plans never exceed one round of resident waves (unless 1 split)
+        assert n == 1 or B * Hkv * (-(-(Hq // Hkv) // 16)) * n <= 2048
+    want_n, chunk = _plan(Skv, req, B, Hkv, Hq)
     assert n == want_n
     assert (n - 1) * chunk < Skv <= n * chunk  # every split non-empty
     rows = B * Hq * n

@@ -23,8 +23,10 @@
 //    of 16 rows cover all banks) and read back transposed with
 //    ds_read_b64_tr_b8 in exactly the token order of the P^T registers; the
 //    codes become the A operand of O^T += V^T P^T.
-//  * the next tile's K, V and scale loads are issued before the current tile
-//    is computed, so HBM streams while the matrix cores work.
+//  * loads run three tiles ahead of use through a four-slot register ring
+//    (about 25 KB in flight per wave), which is what keeps HBM busy: the
+//    kernel is bound by bytes in flight, not by arithmetic.  Scales arrive as
+//    one dword per lane per tile and are redistributed through LDS.
 #include "device_util.h"
 #include "launch.h"
 
@@ -37,6 +39,10 @@ constexpr int kTile = 32;                 // tokens per step of the split kernel
 constexpr float kNegHuge = -1e30f;
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr int kHeadsPerWave = 16;         // N of the 16x16x32 product
+// The accumulator and row sum are kept relative to a reference max that is
+// only raised when the running max exceeds it by more than kLazy (base-2
+// units); the shared reference cancels in the normalisation.
+constexpr float kLazy = 8.f;         // N of the 16x16x32 product
 
 static_assert(kDecodeTile % kTile == 0, "split chunks must hold whole tiles");
 
@@ -59,13 +65,13 @@ struct SplitParams {
 // Loads of one 32-token tile held in registers between issue and use.
 template <int D>
 struct TileRegs {
-  uint4 k[2][D / 64];   // [16-token block][16-byte piece]: token l%16, dims 16*(l/16 + 4u) ..
-  uint4 v[D / 32];      // coalesced rows: 64 lanes x 16 bytes per load
-  f32x4 ksc[2], vsc[2]; // scales of tokens 16*blk + 4*(l/16) + 0..3
+  uint4 k[2][D / 64];   // K codes, MFMA A layout: token 16*blk + l%16, dims 16*(l/16 + 4u) ..
+  uint4 v[D / 32];      // V codes, coalesced: 64 lanes x 16 bytes per load
+  float sc;             // lane l < 32: k scale of token l; lane l >= 32: v scale of token l - 32
 };
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   constexpr int KU = D / 64;              // 16-byte K pieces per token per lane group
   constexpr int KM = D / 32;              // k-steps of the QK product (32 dims each)
   constexpr int VLOADS = D / 32;          // 16-byte V loads per lane per tile
@@ -74,6 +80,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
   constexpr int VSTRIDE = D + 16;         // padded LDS row (bytes)
   constexpr int CB = D / 16;              // 16-dim blocks of the output
   __shared__ __attribute__((aligned(16))) char vlds[kTile * VSTRIDE];
+  __shared__ __attribute__((aligned(16))) float slds[2 * kTile];   // k scales, then v scales
 
   const int lane = threadIdx.x;
   const int n = lane & 15;   // head slot (B/C column), also token row of A
@@ -112,9 +119,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
     }
   }
 
-  // 16-byte scale loads need the stream's scale row to start on a 16-byte boundary
-  const bool scales_aligned = (p.Skv & 3) == 0;
-  auto load_tile = [&](int t0, TileRegs<D>& r) {
+  // Tile loads (plain global loads into registers; tokens past the split end
+  // read as zero).  Issued three tiles ahead of use.
+  const int v_row = lane / CPR, v_col = 16 * (lane % CPR);
+  const float* sc_src = lane < kTile ? ksb : vsb;
+  const int sc_tok = lane & (kTile - 1);
+  auto load_tile = [&](int t, TileRegs<D>& r) __attribute__((always_inline)) {
+    const int t0 = t_begin + t * kTile;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int tok = t0 + 16 * blk + n;
@@ -124,26 +135,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
             ? *reinterpret_cast<const uint4*>(kbase + int64_t(tok) * D + 16 * (g + 4 * u))
             : make_uint4(0u, 0u, 0u, 0u);
       }
-      const int st = t0 + 16 * blk + 4 * g;
-      if (scales_aligned && st + 3 < t_end) {
-        r.ksc[blk] = *reinterpret_cast<const f32x4*>(ksb + st);
-        r.vsc[blk] = *reinterpret_cast<const f32x4*>(vsb + st);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          r.ksc[blk][e] = st + e < t_end ? ksb[st + e] : 0.f;
-          r.vsc[blk][e] = st + e < t_end ? vsb[st + e] : 0.f;
-        }
-      }
     }
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int row = i * RPL + lane / CPR;
-      const int tok = t0 + row;
-      r.v[i] = tok < t_end
-          ? *reinterpret_cast<const uint4*>(vbase + int64_t(tok) * D + 16 * (lane % CPR))
-          : make_uint4(0u, 0u, 0u, 0u);
+      const int tok = t0 + i * RPL + v_row;
+      r.v[i] = tok < t_end ? *reinterpret_cast<const uint4*>(vbase + int64_t(tok) * D + v_col)
+                           : make_uint4(0u, 0u, 0u, 0u);
     }
+    const int stok = t0 + sc_tok;
+    r.sc = stok < t_end ? sc_src[stok] : 0.f;
   };
 
   f32x4 acc[CB];
@@ -151,19 +151,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{};
   float m_run = kNegHuge, l_run = 0.f;
 
-  TileRegs<D> cur, nxt;
-  if (ntiles > 0) load_tile(t_begin, cur);
+  // P^T slot e of lane group g is token 4g + e (e < 4) or 16 + 4g + (e - 4);
+  // source lane s of the group addresses that token's V row (tr8 read).
+  const int s16 = lane & 15;
+  const int e_src = s16 >> 1;
+  const int vrow = e_src < 4 ? 4 * g + e_src : 16 + 4 * g + (e_src - 4);
+  const char* vread = vlds + vrow * VSTRIDE + 8 * (s16 & 1);
 
-  for (int t = 0; t < ntiles; ++t) {
+  auto process = [&](int t, const TileRegs<D>& r) __attribute__((always_inline)) {
     const int t0 = t_begin + t * kTile;
-    if (t + 1 < ntiles) load_tile(t0 + kTile, nxt);
-
-    // stage V codes of this tile (row-major, padded rows)
+    // stage V codes (row-major, padded rows) and the tile's scales
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int row = i * RPL + lane / CPR;
-      *reinterpret_cast<uint4*>(vlds + row * VSTRIDE + 16 * (lane % CPR)) = cur.v[i];
+      *reinterpret_cast<uint4*>(vlds + (i * RPL + v_row) * VSTRIDE + v_col) = r.v[i];
     }
+    slds[lane] = r.sc;
 
     // S = K q^T: rows = tokens 16*blk + 4g + r, columns = head slot n
     f32x4 s[2];
@@ -172,56 +174,78 @@ __global__ __launch_bounds__(64) void decode_split_kernel(SplitParams p) {
       s[blk] = f32x4{};
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
-        const uint4 w = cur.k[blk][m >> 1];
+        const uint4 w = r.k[blk][m >> 1];
         const bf16x8 a = (m & 1) ? i8x8_to_bf16x8(w.z, w.w) : i8x8_to_bf16x8(w.x, w.y);
         s[blk] = mfma16(a, qf[m], s[blk]);
       }
     }
 
-    // scaled scores (base 2), masked past the split end
+    // scaled scores (base 2): the k scale of each token multiplies its score
+    const f32x4 ks0 = *reinterpret_cast<const f32x4*>(slds + 4 * g);
+    const f32x4 ks1 = *reinterpret_cast<const f32x4*>(slds + 16 + 4 * g);
     float tv[8];
-    float mx = kNegHuge;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int rr = 0; rr < 4; ++rr) {
+      tv[rr] = s[0][rr] * (ks0[rr] * p.c);
+      tv[4 + rr] = s[1][rr] * (ks1[rr] * p.c);
+    }
+    if (t0 + kTile > t_end) {  // ragged last tile: tokens past the end are not keys
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = t0 + 16 * blk + 4 * g + r;
-        const float val = s[blk][r] * (cur.ksc[blk][r] * p.c);
-        tv[4 * blk + r] = tok < t_end ? val : -INFINITY;
-        mx = fmaxf(mx, tv[4 * blk + r]);
+      for (int e = 0; e < 8; ++e) {
+        const int tok = t0 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+        if (tok >= t_end) tv[e] = -INFINITY;
       }
     }
+    float mx = kNegHuge;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, tv[e]);
     mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    mx = max_across_halves(mx);
+    if (__builtin_expect(__any(mx > m_run + kLazy), 0)) {  // rare: raise the reference
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
+    }
+    const f32x4 vs0 = *reinterpret_cast<const f32x4*>(slds + kTile + 4 * g);
+    const f32x4 vs1 = *reinterpret_cast<const f32x4*>(slds + kTile + 16 + 4 * g);
     float pv[8];
-    float ls = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(tv[e] - m_new);
-      ls += pe;
-      pv[e] = pe * cur.vsc[e >> 2][e & 3];
+      const float pe = __builtin_amdgcn_exp2f(tv[e] - m_run);
+      l_run += pe;
+      pv[e] = pe * (e < 4 ? vs0[e] : vs1[e - 4]);
     }
-    l_run = l_run * alpha + ls;
     const bf16x8 pf = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
 
-    // O^T += V^T P^T.  P^T slot e of lane group g is token 4g + e (e < 4) or
-    // 16 + 4g + (e - 4); source lane s of the group addresses that token's row.
-    const int s16 = lane & 15;
-    const int e_src = s16 >> 1;
-    const int vrow = e_src < 4 ? 4 * g + e_src : 16 + 4 * g + (e_src - 4);
+    // O^T += V^T P^T with V^T read transposed from the staged tile
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const i32x2 raw = lds_read_tr8(vlds + vrow * VSTRIDE + 16 * cb + 8 * (s16 & 1));
+      const i32x2 raw = lds_read_tr8(vread + 16 * cb);
       const bf16x8 a = i8x8_to_bf16x8(uint32_t(raw[0]), uint32_t(raw[1]));
       acc[cb] = mfma16(a, pf, acc[cb]);
     }
+  };
 
-    if (t + 1 < ntiles) cur = nxt;
+  // four-slot register ring: tiles t+1 .. t+3 are in flight while t is processed
+  TileRegs<D> r0, r1, r2, r3;
+  if (0 < ntiles) load_tile(0, r0);
+  if (1 < ntiles) load_tile(1, r1);
+  if (2 < ntiles) load_tile(2, r2);
+  for (int t = 0; t < ntiles; t += 4) {
+    if (t + 3 < ntiles) load_tile(t + 3, r3);
+    process(t, r0);
+    if (t + 1 >= ntiles) break;
+    if (t + 4 < ntiles) load_tile(t + 4, r0);
+    process(t + 1, r1);
+    if (t + 2 >= ntiles) break;
+    if (t + 5 < ntiles) load_tile(t + 5, r1);
+    process(t + 2, r2);
+    if (t + 3 >= ntiles) break;
+    if (t + 6 < ntiles) load_tile(t + 6, r2);
+    process(t + 3, r3);
   }
 
   // row sum over the four lane groups holding this head's tokens
