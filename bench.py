@@ -301,6 +301,35 @@ def main():
             del qq, kk, vv, oo
         result["prefill_other_workloads"] = others
 
+    if args.only == "all":
+        # next rows of the path, each timed the same way (informational)
+        result["next"] = {}
+        # int8 KV-cache append: quantise one tensor (K) of the decode workload's 32K-token cache
+        del dq, dkq, dks, dvq, dvs
+        torch.cuda.empty_cache()
+        g = torch.Generator(device=dev)
+        g.manual_seed(wd.seed)
+        xk = torch.randn(wd.B, wd.Skv, wd.Hkv, wd.d, generator=g, device=dev).to(torch.bfloat16)
+        codes = torch.empty(wd.B, wd.Hkv, wd.Skv, wd.d, dtype=torch.int8, device=dev)
+        scs = torch.empty(wd.B, wd.Hkv, wd.Skv, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            fa.kv_append_int8(xk, codes, scs, pos=0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            fa.kv_append_int8(xk, codes, scs, pos=0)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = xk.numel() * 2 + codes.numel() + scs.numel() * 4
+        result["next"]["kv_append_int8"] = {
+            "workload": f"append B{wd.B} T{wd.Skv} Hkv{wd.Hkv} d{wd.d} bf16 -> int8 cache",
+            "us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": nbytes}
+        del xk, codes, scs
+
     if do_prefill and not args.no_cpu_baseline:
         log(f"cpu baseline: fp64 oracle, about {args.cpu_budget:.0f} s")
         result["cpu_baseline"] = time_cpu_baseline(wp, q_cpu, k_cpu, v_cpu, args.cpu_budget)

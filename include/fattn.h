@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   FATTN_OK = 0,
   FATTN_EINVAL = -1,      /* a NULL or misaligned pointer, a size < 1,
-                             Hq % Hkv != 0, a
+                             Hq % Hkv != 0, an append past the cache end, a
                              non-finite scale, causal not 0/1, window < 0,
                              window > 0 without causal, num_splits < 0, or a
                              tensor too large to index */
@@ -124,6 +124,23 @@ FATTN_API int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_
                       int B, int Hq, int Hkv, int Skv, int d, float scale,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * Appends T new tokens to an int8 KV cache (the step that fills the cache
+ * fattn_decode_int8 reads; [FA-3MOVES] move 3 names the int8 cache).  For each
+ * (b, t, kv head) row x of d values: scale = absmax(x) / 127 in fp32 and
+ * code_c = clamp(round-half-even(x_c / scale), -127, 127), with IEEE fp32
+ * correctly rounded divisions; an all-zero row gets scale 0 and zero codes.
+ *
+ * x      [B, T, Hkv, d] (the new tokens' K or V in the prefill layout),
+ *        float32 or bfloat16 as dtype says
+ * codes  [B, Hkv, cap, d] int8 cache, scales [B, Hkv, cap] fp32: positions
+ *        pos .. pos+T-1 of every (b, kv head) stream are written, nothing else
+ * Requires 0 <= pos and pos + T <= cap.  d: 64 or 128.
+ */
+FATTN_API int fattn_kv_append_int8(const void* x, int8_t* codes, float* scales,
+                                   int B, int T, int Hkv, int d, int pos, int cap,
+                                   int dtype, void* stream);
 
 /* Number of key splits fattn_decode_int8 will use for these arguments
  * (>= 1), or a negative fattn_status if they are invalid.  Host only. */

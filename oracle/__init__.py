@@ -55,6 +55,8 @@ def _load(path: str | None = None):
         lib.oracle_decode_int8_rows.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                 f64, vp, i64, vp, vp, i32]
         lib.oracle_decode_int8_rows.restype = i32
+        lib.oracle_kv_quantize_int8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
+        lib.oracle_kv_quantize_int8.restype = i32
         lib.oracle_max_threads.argtypes = [i32]
         lib.oracle_max_threads.restype = i32
         _libs[path] = lib
@@ -161,3 +163,33 @@ def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
         o = o.reshape(B, Hq, d)
         lse = lse.reshape(B, Hq)
     return o, lse
+
+
+def kv_quantize_int8(x, codes=None, scales=None, *, pos: int = 0, cap: int | None = None,
+                     lib: str | None = None):
+    """Quantise new tokens x [B, T, Hkv, d] into an int8 cache (see oracle.c).
+
+    codes [B, Hkv, cap, d] int8 and scales [B, Hkv, cap] float32 are updated in
+    place at positions pos .. pos+T-1 (new zero-filled arrays when None).
+    Returns (codes, scales).  x is taken as float32 (exact for bf16 values).
+    """
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").float().numpy()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    B, T, Hkv, d = xa.shape
+    if cap is None:
+        cap = pos + T
+    if codes is None:
+        codes = np.zeros((B, Hkv, cap, d), dtype=np.int8)
+    if scales is None:
+        scales = np.zeros((B, Hkv, cap), dtype=np.float32)
+    if codes.shape != (B, Hkv, cap, d) or scales.shape != (B, Hkv, cap):
+        raise ValueError("cache arrays must be [B, Hkv, cap, d] and [B, Hkv, cap]")
+    if codes.dtype != np.int8 or scales.dtype != np.float32 or not codes.flags.c_contiguous \
+            or not scales.flags.c_contiguous:
+        raise TypeError("codes must be contiguous int8 and scales contiguous float32")
+    rc = _load(lib).oracle_kv_quantize_int8(_ptr(xa), _ptr(codes), _ptr(scales), B, Hkv, T, d,
+                                             int(pos), int(cap))
+    if rc != 0:
+        raise ValueError(f"oracle_kv_quantize_int8 rejected its arguments (code {rc})")
+    return codes, scales

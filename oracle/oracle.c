@@ -235,6 +235,52 @@ int oracle_decode_int8_rows(const double* q, const int8_t* kq, const float* ks,
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
+/*
+ * Appending tokens to the int8 KV cache: for every (b, t, kv head) row x of
+ * d values, scale = absmax(x) / 127 and code_c = clamp(round(x_c / scale),
+ * -127, 127), round-half-to-even; an all-zero row gets scale 0 and codes 0.
+ * This is the per-(token, kv head) symmetric scheme of the int8 workload;
+ * [FA-3MOVES] move 3 names the int8 cache but gives no scheme.  Because the
+ * result is integer, the arithmetic deciding it is the kernel's: IEEE fp32,
+ * one correctly rounded division for the scale and one per element.
+ *   x [B, T, Hkv, d] (float values; bf16 inputs are widened exactly)
+ *   codes [B, Hkv, cap, d] int8, scales [B, Hkv, cap] fp32: positions
+ *   pos .. pos+T-1 are written, everything else is left as it was.
+ */
+int oracle_kv_quantize_int8(const float* x, int8_t* codes, float* scales,
+                            int B, int Hkv, int T, int d, int pos, int cap) {
+  if (B < 1 || Hkv < 1 || T < 1 || d < 1 || pos < 0 || (int64_t)pos + T > cap) return ORACLE_BAD_ARGS;
+  if (!x || !codes || !scales) return ORACLE_BAD_ARGS;
+  for (int64_t b = 0; b < B; b++) {
+    for (int64_t t = 0; t < T; t++) {
+      for (int64_t h = 0; h < Hkv; h++) {
+        const float* row = x + ((b * T + t) * Hkv + h) * (int64_t)d;
+        float amax = 0.0f;
+        for (int c = 0; c < d; c++) {
+          float a = fabsf(row[c]);
+          if (a > amax) amax = a;
+        }
+        volatile float scale = amax / 127.0f; /* stored as fp32, as the cache holds it */
+        int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;
+        scales[slot] = scale;
+        int8_t* out = codes + slot * (int64_t)d;
+        for (int c = 0; c < d; c++) {
+          if (scale == 0.0f) {
+            out[c] = 0;
+            continue;
+          }
+          volatile float qv = row[c] / scale;
+          float r = rintf(qv); /* default rounding mode: to nearest, ties to even */
+          if (r > 127.0f) r = 127.0f;
+          if (r < -127.0f) r = -127.0f;
+          out[c] = (int8_t)r;
+        }
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
 /* Number of threads an OpenMP region will use (for reporting). */
 int oracle_max_threads(int nthreads) {
 #ifdef _OPENMP

@@ -47,7 +47,8 @@ def test_library_is_built_and_loads():
 def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == sorted(["fattn_fwd", "fattn_decode_int8", "fattn_decode_num_splits",
-                            "fattn_decode_workspace_size", "fattn_status_string", "fattn_version"])
+                            "fattn_decode_workspace_size", "fattn_kv_append_int8",
+                            "fattn_status_string", "fattn_version"])
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -174,3 +175,21 @@ def test_torch_wrappers_reject_cpu_tensors():
         fa.fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.fwd(q.half(), q.half(), q.half())
+
+
+def _app(**kw):
+    a = dict(x=P, codes=P, scales=P, B=1, T=4, Hkv=2, d=128, pos=0, cap=8, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fattn_kv_append_int8(a["x"], a["codes"], a["scales"], a["B"], a["T"], a["Hkv"], a["d"],
+                                   a["pos"], a["cap"], a["dtype"], a["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), FATTN_EINVAL), (dict(codes=None), FATTN_EINVAL), (dict(scales=None), FATTN_EINVAL),
+    (dict(scales=P + 4), FATTN_EINVAL), (dict(B=0), FATTN_EINVAL), (dict(T=0), FATTN_EINVAL),
+    (dict(pos=-1), FATTN_EINVAL), (dict(pos=5), FATTN_EINVAL), (dict(T=9), FATTN_EINVAL),
+    (dict(d=96), FATTN_EUNSUPPORTED), (dict(dtype=3), FATTN_EUNSUPPORTED),
+])
+def test_kv_append_rejects_before_any_device_work(kw, want):
+    assert _app(**kw) == want

@@ -378,6 +378,46 @@ def pin_torch_sdpa_float64(lib):
         assert np.allclose(o, ref.permute(0, 2, 1, 3).numpy(), atol=1e-12, rtol=0)
 
 
+def pin_quantizer_rounding_and_bounds(lib):
+    # absmax 127 gives scale exactly 1: codes are round-half-even of the values
+    x = np.zeros((1, 1, 1, 8), dtype=np.float32)
+    x[0, 0, 0] = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5, -126.5, 1.25]
+    c, sc = oracle.kv_quantize_int8(x, lib=lib)
+    assert sc[0, 0, 0] == np.float32(1.0)
+    assert list(c[0, 0, 0]) == [127, 2, 4, -2, -4, 0, -126, 1]
+    # general rows: the absmax element maps to +-127, the error is at most half a step
+    rng = np.random.default_rng(50)
+    x = rng.standard_normal((2, 5, 3, 16)).astype(np.float32) * rng.uniform(0.01, 100, (2, 5, 3, 1)).astype(np.float32)
+    x[1, 2, 1] = 0.0  # an all-zero row
+    codes = np.full((2, 3, 9, 16), 77, dtype=np.int8)
+    scales = np.full((2, 3, 9), -1.0, dtype=np.float32)
+    oracle.kv_quantize_int8(x, codes, scales, pos=3, cap=9, lib=lib)
+    assert np.all(codes[:, :, :3] == 77) and np.all(codes[:, :, 8:] == 77)  # untouched
+    assert np.all(scales[:, :, :3] == -1) and np.all(scales[:, :, 8:] == -1)
+    got_c = codes[:, :, 3:8].transpose(0, 2, 1, 3)  # -> [B, T, Hkv, d]
+    got_s = scales[:, :, 3:8].transpose(0, 2, 1)
+    assert got_s[1, 2, 1] == 0 and np.all(got_c[1, 2, 1] == 0)
+    amax = np.abs(x).max(-1)
+    nz = amax > 0
+    assert np.all(np.abs(got_c[nz].astype(int)).max(-1) == 127)
+    assert np.all(np.abs(got_c.astype(int)) <= 127)
+    deq = got_c.astype(np.float64) * got_s[..., None].astype(np.float64)
+    assert np.all(np.abs(deq - x) <= 0.5 * got_s[..., None] * (1 + 1e-6) + 1e-30)
+    assert np.allclose(got_s[nz], amax[nz] / 127.0, rtol=1e-7, atol=0)
+
+
+def pin_quantizer_matches_torch(lib):
+    # an independent implementation of the same fp32 recipe (torch ops, CPU)
+    import workloads as W
+    g = torch.Generator().manual_seed(51)
+    x = torch.randn(3, 7, 4, 64, generator=g) * 3
+    x[0, 1, 2] = 0
+    c_ref, s_ref = W.quantize_rows_int8(x)  # over the last axis, rows (b, t, h)
+    c, sc = oracle.kv_quantize_int8(x.numpy(), lib=lib)
+    assert np.array_equal(c.transpose(0, 2, 1, 3), c_ref.numpy())
+    assert np.array_equal(sc.transpose(0, 2, 1), s_ref.numpy())
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -407,6 +447,10 @@ MUTANTS = {
     "top-left causal alignment": ("int64_t off = (int64_t)Skv - (int64_t)Sq;", "int64_t off = 0;"),
     "decode ignores k scale": ("double sc = (double)ks[j];", "double sc = 1.0;"),
     "decode v uses k codes": ("const int8_t* vr = vq + j * (int64_t)d;", "const int8_t* vr = kq + j * (int64_t)d;"),
+    "quantiser step absmax/128": ("volatile float scale = amax / 127.0f;", "volatile float scale = amax / 128.0f;"),
+    "quantiser rounds half away from zero": ("float r = rintf(qv);", "float r = roundf(qv);"),
+    "quantiser ignores the append position": ("int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;",
+                                             "int64_t slot = (b * Hkv + h) * (int64_t)cap + t;"),
 }
 
 

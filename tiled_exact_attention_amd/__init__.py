@@ -21,9 +21,11 @@ from ._binding import (  # noqa: F401
     fattn_decode_num_splits,
     fattn_decode_workspace_size,
     fattn_fwd,
+    fattn_kv_append_int8,
     fattn_status_string,
     fattn_version,
     fwd,
+    kv_append_int8,
     library_path,
     load,
 )

@@ -49,6 +49,8 @@ def load():
         lib.fattn_decode_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                           f32, i32, vp, sz, vp]
         lib.fattn_decode_int8.restype = i32
+        lib.fattn_kv_append_int8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+        lib.fattn_kv_append_int8.restype = i32
         lib.fattn_decode_num_splits.argtypes = [i32] * 6
         lib.fattn_decode_num_splits.restype = i32
         lib.fattn_decode_workspace_size.argtypes = [i32] * 6
@@ -72,6 +74,10 @@ def fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, s
                       num_splits, workspace, workspace_bytes, stream) -> int:
     return load().fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d,
                                     scale, num_splits, workspace, workspace_bytes, stream)
+
+
+def fattn_kv_append_int8(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream) -> int:
+    return load().fattn_kv_append_int8(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream)
 
 
 def fattn_decode_num_splits(B, Hq, Hkv, Skv, d, num_splits) -> int:
@@ -209,3 +215,26 @@ def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_
     if st != 0:
         raise FattnError(st, "fattn_decode_int8")
     return (out, lse) if return_lse else out
+
+
+def kv_append_int8(x, codes, scales, *, pos: int):
+    """Quantise new tokens x [B, T, Hkv, d] (float32 or bfloat16) into the int8
+    cache codes [B, Hkv, cap, d] / scales [B, Hkv, cap] at positions pos .. pos+T-1
+    (see fattn_kv_append_int8).  Updates codes and scales in place and returns them."""
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _check(x, "x", x.dtype, 4)
+    _check(codes, "codes", torch.int8, 4, x.device)
+    _check(scales, "scales", torch.float32, 3, x.device)
+    B, T, Hkv, d = x.shape
+    Bc, Hc, cap, dc = codes.shape
+    if (Bc, Hc, dc) != (B, Hkv, d) or tuple(scales.shape) != (B, Hkv, cap):
+        raise ValueError(f"cache shapes {tuple(codes.shape)}, {tuple(scales.shape)} do not match x {tuple(x.shape)}")
+    with torch.cuda.device(x.device):
+        st = fattn_kv_append_int8(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, T, Hkv, d,
+                                  int(pos), cap, FATTN_F32 if x.dtype == torch.float32 else FATTN_BF16,
+                                  _stream_of(x.device))
+    if st != 0:
+        raise FattnError(st, "fattn_kv_append_int8")
+    return codes, scales

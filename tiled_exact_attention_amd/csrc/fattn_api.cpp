@@ -152,6 +152,21 @@ int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_scale,
   return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
 }
 
+int fattn_kv_append_int8(const void* x, int8_t* codes, float* scales,
+                         int B, int T, int Hkv, int d, int pos, int cap, int dtype, void* stream) {
+  if (!x || !codes || !scales) return FATTN_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FATTN_EINVAL;
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || pos < 0 || cap < 1) return FATTN_EINVAL;
+  if (int64_t(pos) + T > cap) return FATTN_EINVAL;
+  if (!fits(B, T, Hkv, d) || !fits(B, Hkv, cap, d)) return FATTN_EINVAL;
+  if (int64_t(B) * T * Hkv > int64_t(0x7fffffff) * 16) return FATTN_EINVAL;
+  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
+  if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
+  fattn::KvQuantArgs a{x, codes, scales, B, T, Hkv, d, pos, cap, dtype == FATTN_BF16};
+  hipError_t err = fattn::launch_kv_quant(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+}
+
 const char* fattn_status_string(int status) {
   switch (status) {
     case FATTN_OK: return "ok";

@@ -38,9 +38,19 @@ struct DecodeArgs {
   float* part_lse;        // workspace: [B, Hq, nsplit] fp32
 };
 
+// Arguments of one int8 KV-cache append after validation.
+struct KvQuantArgs {
+  const void* x;          // [B, T, Hkv, d] bf16 or fp32
+  int8_t* codes;          // [B, Hkv, cap, d]
+  float* scales;          // [B, Hkv, cap]
+  int B, T, Hkv, d, pos, cap;
+  bool bf16;
+};
+
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_kv_quant(const KvQuantArgs& a, hipStream_t stream);
 
 // Key-tile length of the decode split kernel; split chunks are multiples of it.
 constexpr int kDecodeTile = 64;
