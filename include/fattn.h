@@ -136,7 +136,8 @@ FATTN_API int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_
  *        float32 or bfloat16 as dtype says
  * codes  [B, Hkv, cap, d] int8 cache, scales [B, Hkv, cap] fp32: positions
  *        pos .. pos+T-1 of every (b, kv head) stream are written, nothing else
- * Requires 0 <= pos and pos + T <= cap.  d: 64 or 128.
+ * Requires 0 <= pos and pos + T <= cap.  d: 64 or 128.  x must be finite
+ * (non-finite values give unspecified codes, never a fault).
  */
 FATTN_API int fattn_kv_append_int8(const void* x, int8_t* codes, float* scales,
                                    int B, int T, int Hkv, int d, int pos, int cap,

@@ -4,15 +4,26 @@
 // fp32 scale: scale = absmax(x) / 127, code = clamp(rint(x / scale), -127,
 // 127) with ties to even, an all-zero row giving scale 0 and zero codes (the
 // per-token, per-head symmetric scheme of the int8 cache; [FA-3MOVES] move 3
-// names the cache, not a scheme).  The codes decide integers, so the
-// arithmetic is exactly the one the cache format is defined by: IEEE fp32
-// with correctly rounded divisions (no reciprocal approximation).
+// names the cache, not a scheme).  The codes decide integers, so every
+// quotient x / scale is the correctly rounded IEEE fp32 one.
+//
+// Division: one correctly rounded reciprocal y = 1/scale per row, then per
+// element q0 = x*y, r = fma(-q0, scale, x) (exact) and q = fma(r, y, q0),
+// which is the correctly rounded quotient by Markstein's theorem (IBM J. Res.
+// Dev. 34(1), 1990: y within half an ulp of 1/b, q0 within one ulp of a/b)
+// as long as r stays a normal number for every quotient that can round to a
+// non-zero code.  That holds for 2^-100 <= scale <= 2^120, which covers every
+// finite row with absmax >= 2^-93; other rows take plain IEEE divisions.
 //
 // gfx950: the kernel is HBM-bound (2 or 4 bytes read and 1 written per
-// element).  A row is handled by d/8 consecutive lanes, 8 values each (one
-// 16-byte bf16 load or two fp32 loads), the row's absmax reduced with
-// cross-lane xor shuffles; each lane stores its 8 codes as one 8-byte write
-// into the head-major cache, the row's first lane the scale.
+// element).  A row is handled by d/8 consecutive lanes, 8 values each; every
+// lane group takes kRows rows spaced one block-pass apart and issues all their
+// loads before any arithmetic, so each lane keeps 4-8 16-byte loads in
+// flight.  The row's absmax is reduced with cross-lane xor shuffles; each lane
+// stores its 8 codes as one 8-byte write into the head-major cache, the row's
+// first lane the scale.
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 
@@ -20,69 +31,100 @@ namespace fattn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kRows = 4;  // rows per lane group
 
-template <int D, typename T>
+// I: row-index type, 32-bit whenever B*T*Hkv fits (the 64-bit divisions that
+// map a row to its cache slot are emulated and cost ~10x more)
+template <int D, typename T, typename I>
 __global__ __launch_bounds__(kThreads) void kv_quant_kernel(const T* __restrict__ x,
                                                             int8_t* __restrict__ codes,
                                                             float* __restrict__ scales,
                                                             int64_t rows, int Tn, int Hkv,
                                                             int pos, int cap) {
-  constexpr int L = D / 8;                     // lanes per row
-  constexpr int RPB = kThreads / L;            // rows per block
+  constexpr int L = D / 8;              // lanes per row
+  constexpr int RPP = kThreads / L;     // rows per block pass
   const int lane_in_row = threadIdx.x % L;
-  const int64_t r = int64_t(blockIdx.x) * RPB + threadIdx.x / L;  // row = (b, t, h)
-  const bool live = r < rows;
-  const int64_t rr = live ? r : 0;
-  const int h = int(rr % Hkv);
-  const int64_t bt = rr / Hkv;
-  const int t = int(bt % Tn);
-  const int64_t b = bt / Tn;
+  const int64_t r0 = int64_t(blockIdx.x) * (RPP * kRows) + threadIdx.x / L;
 
-  float v[8];
-  const T* src = x + rr * D + 8 * lane_in_row;
-  if constexpr (sizeof(T) == 2) {
-    const bf16x8 raw = *reinterpret_cast<const bf16x8*>(src);
+  // raw bits first: all loads in flight before any arithmetic
+  using Raw = typename std::conditional<sizeof(T) == 2, bf16x8, f32x4>::type;
+  constexpr int kLoads = sizeof(T) == 2 ? 1 : 2;
+  Raw raw[kRows][kLoads];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = float(raw[e]);
-  } else {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-    const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
+  for (int i = 0; i < kRows; ++i) {
+    const int64_t r = r0 + int64_t(i) * RPP;
+    const T* src = x + (r < rows ? r : 0) * D + 8 * lane_in_row;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = c[e]; }
+    for (int j = 0; j < kLoads; ++j) raw[i][j] = reinterpret_cast<const Raw*>(src)[j];
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
-#pragma unroll
-  for (int m = 1; m < L; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-  const float scale = amax / 127.0f;
 
-  uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float q = 0.f;
-    if (scale != 0.f) {
-      q = __builtin_rintf(v[e] / scale);
-      q = fminf(fmaxf(q, -127.f), 127.f);
+  for (int i = 0; i < kRows; ++i) {
+    const int64_t r = r0 + int64_t(i) * RPP;
+    float v[8];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = float(raw[i][0][e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { v[e] = raw[i][0][e]; v[4 + e] = raw[i][1][e]; }
     }
-    const uint32_t byte = uint32_t(int32_t(q)) & 0xffu;
-    if (e < 4) lo |= byte << (8 * e); else hi |= byte << (8 * (e - 4));
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    const float scale = amax / 127.0f;
+    const float y = 1.0f / scale;
+    const bool exact_fma = scale >= 0x1p-100f && scale <= 0x1p120f;
+
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q0 = v[e] * y;
+      q[e] = __builtin_fmaf(__builtin_fmaf(-q0, scale, v[e]), y, q0);
+    }
+    if (__builtin_expect(!exact_fma, 0)) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = scale != 0.f ? v[e] / scale : 0.f;
+    }
+    // clamp, then round half to even by adding 1.5 * 2^23: the sum's ulp is 1,
+    // so its low mantissa byte is the code in two's complement
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = __builtin_amdgcn_fmed3f(q[e], -127.f, 127.f) + 12582912.0f;
+      const uint32_t byte = __float_as_uint(c) & 0xffu;
+      if (e < 4) lo |= byte << (8 * e); else hi |= byte << (8 * (e - 4));
+    }
+    if (r < rows) {
+      const I ri = I(r);
+      const I bt = ri / I(Hkv);
+      const I h = ri - bt * I(Hkv);
+      const I b = bt / I(Tn);
+      const I t = bt - b * I(Tn);
+      const int64_t slot = (int64_t(b) * Hkv + int64_t(h)) * int64_t(cap) + pos + int64_t(t);
+      *reinterpret_cast<uint2*>(codes + slot * D + 8 * lane_in_row) = make_uint2(lo, hi);
+      if (lane_in_row == 0) scales[slot] = scale;
+    }
   }
-  if (!live) return;
-  const int64_t slot = (b * Hkv + h) * int64_t(cap) + pos + t;
-  *reinterpret_cast<uint2*>(codes + slot * D + 8 * lane_in_row) = make_uint2(lo, hi);
-  if (lane_in_row == 0) scales[slot] = scale;
+}
+
+template <int D, typename T, typename I>
+hipError_t launch_idx(const KvQuantArgs& a, int64_t rows, hipStream_t stream) {
+  constexpr int RPB = kThreads / (D / 8) * kRows;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((kv_quant_kernel<D, T, I>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<const T*>(a.x), a.codes, a.scales, rows, a.T, a.Hkv, a.pos, a.cap);
+  return hipGetLastError();
 }
 
 template <int D, typename T>
 hipError_t launch(const KvQuantArgs& a, hipStream_t stream) {
-  constexpr int RPB = kThreads / (D / 8);
   const int64_t rows = int64_t(a.B) * a.T * a.Hkv;
-  const int64_t blocks = (rows + RPB - 1) / RPB;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((kv_quant_kernel<D, T>), dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
-                     static_cast<const T*>(a.x), a.codes, a.scales, rows, a.T, a.Hkv, a.pos, a.cap);
-  return hipGetLastError();
+  if (rows <= 0xffffffffll) return launch_idx<D, T, uint32_t>(a, rows, stream);
+  return launch_idx<D, T, uint64_t>(a, rows, stream);
 }
 
 }  // namespace
