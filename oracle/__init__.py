@@ -55,8 +55,12 @@ def _load(path: str | None = None):
         lib.oracle_decode_int8_rows.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                 f64, vp, i64, vp, vp, i32]
         lib.oracle_decode_int8_rows.restype = i32
+        lib.oracle_decode_int4_rows.argtypes = lib.oracle_decode_int8_rows.argtypes
+        lib.oracle_decode_int4_rows.restype = i32
         lib.oracle_kv_quantize_int8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
         lib.oracle_kv_quantize_int8.restype = i32
+        lib.oracle_kv_quantize_int4.argtypes = lib.oracle_kv_quantize_int8.argtypes
+        lib.oracle_kv_quantize_int4.restype = i32
         lib.oracle_max_threads.argtypes = [i32]
         lib.oracle_max_threads.restype = i32
         _libs[path] = lib
@@ -125,22 +129,14 @@ def fwd(q, k, v, *, causal: bool, window: int = 0, scale: float | None = None,
     return o, lse
 
 
-def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
-                rows=None, threads: int = 0, lib: str | None = None):
-    """Decode attention of one query token over an int8 KV cache, in fp64.
-
-    q: [B, Hq, d] (widened to fp64); kq, vq: [B, Hkv, Skv, d] int8;
-    k_scale, v_scale: [B, Hkv, Skv] float32.  Every cached key is visible.
-    rows: None for all (b, h), else an int array [n, 2] of (b, h) pairs.
-    Returns (o, lse) shaped [B, Hq, d] and [B, Hq], or [n, d] and [n].
-    lib: path of an alternative build of the oracle source (tests only).
-    """
+def _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, bits):
     qd = _f64(q)
-    kqa, vqa = _np(kq, np.int8), _np(vq, np.int8)
+    code_t = np.int8 if bits == 8 else np.uint8
+    kqa, vqa = _np(kq, code_t), _np(vq, code_t)
     ksa, vsa = _np(k_scale, np.float32), _np(v_scale, np.float32)
     B, Hq, d = qd.shape
-    Bk, Hkv, Skv, dk = kqa.shape
-    if (Bk, dk) != (B, d) or vqa.shape != kqa.shape:
+    Bk, Hkv, Skv, rb = kqa.shape
+    if Bk != B or rb * (8 // bits) != d or vqa.shape != kqa.shape:
         raise ValueError("shape mismatch between q and the cache")
     if ksa.shape != (B, Hkv, Skv) or vsa.shape != (B, Hkv, Skv):
         raise ValueError("scale arrays must be [B, Hkv, Skv]")
@@ -154,15 +150,63 @@ def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
     n = rows.shape[0]
     o = np.empty((n, d), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
-    rc = _load(lib).oracle_decode_int8_rows(_ptr(qd), _ptr(kqa), _ptr(ksa), _ptr(vqa), _ptr(vsa),
-                                         B, Hq, Hkv, Skv, d, float(scale),
-                                         _ptr(rows), n, _ptr(o), _ptr(lse), int(threads))
+    fn = _load(lib).oracle_decode_int8_rows if bits == 8 else _load(lib).oracle_decode_int4_rows
+    rc = fn(_ptr(qd), _ptr(kqa), _ptr(ksa), _ptr(vqa), _ptr(vsa), B, Hq, Hkv, Skv, d, float(scale),
+            _ptr(rows), n, _ptr(o), _ptr(lse), int(threads))
     if rc != 0:
-        raise ValueError(f"oracle_decode_int8_rows rejected its arguments (code {rc})")
+        raise ValueError(f"oracle decode (int{bits}) rejected its arguments (code {rc})")
     if full:
         o = o.reshape(B, Hq, d)
         lse = lse.reshape(B, Hq)
     return o, lse
+
+
+def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
+                rows=None, threads: int = 0, lib: str | None = None):
+    """Decode attention of one query token over an int8 KV cache, in fp64.
+
+    q: [B, Hq, d] (widened to fp64); kq, vq: [B, Hkv, Skv, d] int8;
+    k_scale, v_scale: [B, Hkv, Skv] float32.  Every cached key is visible.
+    rows: None for all (b, h), else an int array [n, 2] of (b, h) pairs.
+    Returns (o, lse) shaped [B, Hq, d] and [B, Hq], or [n, d] and [n].
+    lib: path of an alternative build of the oracle source (tests only).
+    """
+    return _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, 8)
+
+
+def decode_int4(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
+                rows=None, threads: int = 0, lib: str | None = None):
+    """Decode attention over an int4 KV cache, in fp64 (as decode_int8).
+
+    kq, vq: [B, Hkv, Skv, d/2] uint8, two signed 4-bit codes per byte
+    (element 2i in the low nibble of byte i, element 2i+1 in the high one).
+    """
+    return _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, 4)
+
+
+def _kv_quantize(x, codes, scales, pos, cap, lib, bits):
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").float().numpy()
+    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    B, T, Hkv, d = xa.shape
+    rb = d if bits == 8 else d // 2
+    code_t = np.int8 if bits == 8 else np.uint8
+    if cap is None:
+        cap = pos + T
+    if codes is None:
+        codes = np.zeros((B, Hkv, cap, rb), dtype=code_t)
+    if scales is None:
+        scales = np.zeros((B, Hkv, cap), dtype=np.float32)
+    if codes.shape != (B, Hkv, cap, rb) or scales.shape != (B, Hkv, cap):
+        raise ValueError("cache arrays must be [B, Hkv, cap, row bytes] and [B, Hkv, cap]")
+    if codes.dtype != code_t or scales.dtype != np.float32 or not codes.flags.c_contiguous \
+            or not scales.flags.c_contiguous:
+        raise TypeError(f"codes must be contiguous {np.dtype(code_t)} and scales contiguous float32")
+    fn = _load(lib).oracle_kv_quantize_int8 if bits == 8 else _load(lib).oracle_kv_quantize_int4
+    rc = fn(_ptr(xa), _ptr(codes), _ptr(scales), B, Hkv, T, d, int(pos), int(cap))
+    if rc != 0:
+        raise ValueError(f"oracle quantiser (int{bits}) rejected its arguments (code {rc})")
+    return codes, scales
 
 
 def kv_quantize_int8(x, codes=None, scales=None, *, pos: int = 0, cap: int | None = None,
@@ -173,23 +217,11 @@ def kv_quantize_int8(x, codes=None, scales=None, *, pos: int = 0, cap: int | Non
     place at positions pos .. pos+T-1 (new zero-filled arrays when None).
     Returns (codes, scales).  x is taken as float32 (exact for bf16 values).
     """
-    if hasattr(x, "detach"):
-        x = x.detach().to("cpu").float().numpy()
-    xa = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    B, T, Hkv, d = xa.shape
-    if cap is None:
-        cap = pos + T
-    if codes is None:
-        codes = np.zeros((B, Hkv, cap, d), dtype=np.int8)
-    if scales is None:
-        scales = np.zeros((B, Hkv, cap), dtype=np.float32)
-    if codes.shape != (B, Hkv, cap, d) or scales.shape != (B, Hkv, cap):
-        raise ValueError("cache arrays must be [B, Hkv, cap, d] and [B, Hkv, cap]")
-    if codes.dtype != np.int8 or scales.dtype != np.float32 or not codes.flags.c_contiguous \
-            or not scales.flags.c_contiguous:
-        raise TypeError("codes must be contiguous int8 and scales contiguous float32")
-    rc = _load(lib).oracle_kv_quantize_int8(_ptr(xa), _ptr(codes), _ptr(scales), B, Hkv, T, d,
-                                             int(pos), int(cap))
-    if rc != 0:
-        raise ValueError(f"oracle_kv_quantize_int8 rejected its arguments (code {rc})")
-    return codes, scales
+    return _kv_quantize(x, codes, scales, pos, cap, lib, 8)
+
+
+def kv_quantize_int4(x, codes=None, scales=None, *, pos: int = 0, cap: int | None = None,
+                     lib: str | None = None):
+    """Quantise new tokens into an int4 cache: scale = absmax/7, codes in [-7, 7],
+    codes [B, Hkv, cap, d/2] uint8 packed two per byte (see oracle.c)."""
+    return _kv_quantize(x, codes, scales, pos, cap, lib, 4)

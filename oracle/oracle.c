@@ -45,6 +45,11 @@
  *    kernel): the cache stores int8 codes and one fp32 scale per (token,
  *    kv head); the value attention sees is code * scale, formed here in
  *    double on the fly.
+ *  - int4 KV cache (the same move taken one step further: two codes per
+ *    byte, one fp32 scale per (token, kv head)): element 2i of a row is the
+ *    low nibble of byte i and element 2i+1 the high nibble, each a signed
+ *    4-bit two's complement number; the pages give no packing, this is a
+ *    reading.
  */
 #include <math.h>
 #include <stdint.h>
@@ -64,14 +69,25 @@ static int bad_shape(int B, int Hq, int Hkv, int Sq, int Skv, int d) {
   return 0;
 }
 
+/* Code of element c of one row of a quantised cache (bits = 8 or 4, see the
+ * readings above). */
+static double code_value(const uint8_t* row, int c, int bits) {
+  if (bits == 8) return (double)(int8_t)row[c];
+  int nib = (c % 2 == 0) ? (int)(row[c / 2] & 15u) : (int)(row[c / 2] >> 4);
+  if (nib >= 8) nib -= 16;
+  return (double)nib;
+}
+
 /* One output row by the three passes above.  s is caller scratch of Skv
- * doubles.  kv_at(j) returns pointers to key/value row j; scale factors of a
- * quantised cache are passed through kscale/vscale (1.0 for plain inputs). */
+ * doubles.  Plain inputs come as double rows kbase/vbase (kv_stride apart);
+ * a quantised cache as code rows kq/vq of row_bytes bytes with per-row
+ * scales ks/vs, each element being code * scale. */
 static void attend_row(const double* qrow, int d, double scale,
                        int64_t jlo, int64_t jhi,
                        const double* kbase, const double* vbase, int64_t kv_stride,
-                       const int8_t* kq, const int8_t* vq, const float* ks, const float* vs,
-                       double* s, double* orow, double* lse_out) {
+                       const uint8_t* kq, const uint8_t* vq, const float* ks, const float* vs,
+                       int bits, double* s, double* orow, double* lse_out) {
+  const int64_t row_bytes = bits == 8 ? d : d / 2;
   int c;
   int64_t j;
   if (jhi <= jlo) {
@@ -87,9 +103,9 @@ static void attend_row(const double* qrow, int d, double scale,
       const double* kr = kbase + j * kv_stride;
       for (c = 0; c < d; c++) acc += qrow[c] * kr[c];
     } else {
-      const int8_t* kr = kq + j * (int64_t)d;
+      const uint8_t* kr = kq + j * row_bytes;
       double sc = (double)ks[j];
-      for (c = 0; c < d; c++) acc += qrow[c] * ((double)kr[c] * sc);
+      for (c = 0; c < d; c++) acc += qrow[c] * (code_value(kr, c, bits) * sc);
     }
     s[j - jlo] = scale * acc;
     if (s[j - jlo] > m) m = s[j - jlo];
@@ -108,9 +124,9 @@ static void attend_row(const double* qrow, int d, double scale,
       const double* vr = vbase + j * kv_stride;
       for (c = 0; c < d; c++) orow[c] += p * vr[c];
     } else {
-      const int8_t* vr = vq + j * (int64_t)d;
+      const uint8_t* vr = vq + j * row_bytes;
       double sc = (double)vs[j];
-      for (c = 0; c < d; c++) orow[c] += p * ((double)vr[c] * sc);
+      for (c = 0; c < d; c++) orow[c] += p * (code_value(vr, c, bits) * sc);
     }
   }
   *lse_out = m + log(l);
@@ -179,7 +195,7 @@ int oracle_fwd_rows(const double* q, const double* k, const double* v,
       int64_t kv_stride = (int64_t)Hkv * d;
       const double* kb = k + (b * Skv * Hkv + hk) * (int64_t)d;
       const double* vb = v + (b * Skv * Hkv + hk) * (int64_t)d;
-      attend_row(qrow, d, scale, jlo, jhi, kb, vb, kv_stride, NULL, NULL, NULL, NULL,
+      attend_row(qrow, d, scale, jlo, jhi, kb, vb, kv_stride, NULL, NULL, NULL, NULL, 0,
                  s, o + r * (int64_t)d, lse + r);
     }
     free(s);
@@ -188,23 +204,26 @@ int oracle_fwd_rows(const double* q, const double* k, const double* v,
 }
 
 /*
- * Decode over an int8 KV cache: one new query token per sequence, every
+ * Decode over a quantised KV cache: one new query token per sequence, every
  * cached key visible.  Layouts:
- *   q [B, Hq, d];  kq, vq [B, Hkv, Skv, d] int8;  ks, vs [B, Hkv, Skv] fp32.
+ *   q [B, Hq, d];  kq, vq [B, Hkv, Skv, row_bytes] codes (row_bytes = d for
+ *   int8, d/2 for int4);  ks, vs [B, Hkv, Skv] fp32.
  * rows: nrows pairs (b, h).  o: nrows x d, lse: nrows.
  */
-int oracle_decode_int8_rows(const double* q, const int8_t* kq, const float* ks,
-                            const int8_t* vq, const float* vs,
-                            int B, int Hq, int Hkv, int Skv, int d, double scale,
-                            const int64_t* rows, int64_t nrows,
-                            double* o, double* lse, int nthreads) {
+static int decode_rows(const double* q, const uint8_t* kq, const float* ks,
+                       const uint8_t* vq, const float* vs,
+                       int B, int Hq, int Hkv, int Skv, int d, double scale,
+                       const int64_t* rows, int64_t nrows,
+                       double* o, double* lse, int nthreads, int bits) {
   if (bad_shape(B, Hq, Hkv, 1, Skv, d)) return ORACLE_BAD_ARGS;
+  if (bits == 4 && d % 2 != 0) return ORACLE_BAD_ARGS;
   if (!q || !kq || !ks || !vq || !vs || !rows || !o || !lse || nrows < 0) return ORACLE_BAD_ARGS;
   for (int64_t r = 0; r < nrows; r++) {
     int64_t b = rows[2 * r], h = rows[2 * r + 1];
     if (b < 0 || b >= B || h < 0 || h >= Hq) return ORACLE_BAD_ARGS;
   }
   int group = Hq / Hkv;
+  int64_t row_bytes = bits == 8 ? d : d / 2;
   int failed = 0;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -226,8 +245,8 @@ int oracle_decode_int8_rows(const double* q, const int8_t* kq, const float* ks,
       int64_t stream = b * Hkv + hk;
       const double* qrow = q + (b * Hq + h) * (int64_t)d;
       attend_row(qrow, d, scale, 0, Skv, NULL, NULL, 0,
-                 kq + stream * Skv * (int64_t)d, vq + stream * Skv * (int64_t)d,
-                 ks + stream * Skv, vs + stream * Skv,
+                 kq + stream * Skv * row_bytes, vq + stream * Skv * row_bytes,
+                 ks + stream * Skv, vs + stream * Skv, bits,
                  s, o + r * (int64_t)d, lse + r);
     }
     free(s);
@@ -235,22 +254,46 @@ int oracle_decode_int8_rows(const double* q, const int8_t* kq, const float* ks,
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
+/* int8 cache: kq, vq [B, Hkv, Skv, d] int8. */
+int oracle_decode_int8_rows(const double* q, const int8_t* kq, const float* ks,
+                            const int8_t* vq, const float* vs,
+                            int B, int Hq, int Hkv, int Skv, int d, double scale,
+                            const int64_t* rows, int64_t nrows,
+                            double* o, double* lse, int nthreads) {
+  return decode_rows(q, (const uint8_t*)kq, ks, (const uint8_t*)vq, vs, B, Hq, Hkv, Skv, d, scale,
+                     rows, nrows, o, lse, nthreads, 8);
+}
+
+/* int4 cache: kq, vq [B, Hkv, Skv, d/2] bytes, two codes each; d even. */
+int oracle_decode_int4_rows(const double* q, const uint8_t* kq, const float* ks,
+                            const uint8_t* vq, const float* vs,
+                            int B, int Hq, int Hkv, int Skv, int d, double scale,
+                            const int64_t* rows, int64_t nrows,
+                            double* o, double* lse, int nthreads) {
+  return decode_rows(q, kq, ks, vq, vs, B, Hq, Hkv, Skv, d, scale, rows, nrows, o, lse, nthreads, 4);
+}
+
 /*
- * Appending tokens to the int8 KV cache: for every (b, t, kv head) row x of
- * d values, scale = absmax(x) / 127 and code_c = clamp(round(x_c / scale),
- * -127, 127), round-half-to-even; an all-zero row gets scale 0 and codes 0.
- * This is the per-(token, kv head) symmetric scheme of the int8 workload;
- * [FA-3MOVES] move 3 names the int8 cache but gives no scheme.  Because the
- * result is integer, the arithmetic deciding it is the kernel's: IEEE fp32,
- * one correctly rounded division for the scale and one per element.
+ * Appending tokens to a quantised KV cache: for every (b, t, kv head) row x
+ * of d values, scale = absmax(x) / qmax and code_c = clamp(round(x_c /
+ * scale), -qmax, qmax), round-half-to-even; an all-zero row gets scale 0
+ * and codes 0.  qmax is 127 for the int8 cache and 7 for the int4 cache.
+ * This is the per-(token, kv head) symmetric scheme of the quantised
+ * workloads; [FA-3MOVES] move 3 names the int8 cache but gives no scheme.
+ * Because the result is integer, the arithmetic deciding it is the kernel's:
+ * IEEE fp32, one correctly rounded division for the scale and one per
+ * element.
  *   x [B, T, Hkv, d] (float values; bf16 inputs are widened exactly)
- *   codes [B, Hkv, cap, d] int8, scales [B, Hkv, cap] fp32: positions
+ *   codes [B, Hkv, cap, row_bytes] (int8: d bytes; int4: d/2 bytes packed
+ *   as in the readings above), scales [B, Hkv, cap] fp32: positions
  *   pos .. pos+T-1 are written, everything else is left as it was.
  */
-int oracle_kv_quantize_int8(const float* x, int8_t* codes, float* scales,
-                            int B, int Hkv, int T, int d, int pos, int cap) {
+static int kv_quantize(const float* x, uint8_t* codes, float* scales,
+                       int B, int Hkv, int T, int d, int pos, int cap, float qmax, int bits) {
   if (B < 1 || Hkv < 1 || T < 1 || d < 1 || pos < 0 || (int64_t)pos + T > cap) return ORACLE_BAD_ARGS;
+  if (bits == 4 && d % 2 != 0) return ORACLE_BAD_ARGS;
   if (!x || !codes || !scales) return ORACLE_BAD_ARGS;
+  int64_t row_bytes = bits == 8 ? d : d / 2;
   for (int64_t b = 0; b < B; b++) {
     for (int64_t t = 0; t < T; t++) {
       for (int64_t h = 0; h < Hkv; h++) {
@@ -260,25 +303,45 @@ int oracle_kv_quantize_int8(const float* x, int8_t* codes, float* scales,
           float a = fabsf(row[c]);
           if (a > amax) amax = a;
         }
-        volatile float scale = amax / 127.0f; /* stored as fp32, as the cache holds it */
+        volatile float scale = amax / qmax; /* stored as fp32, as the cache holds it */
         int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;
         scales[slot] = scale;
-        int8_t* out = codes + slot * (int64_t)d;
+        uint8_t* out = codes + slot * row_bytes;
+        if (bits == 4) {
+          for (int64_t i = 0; i < row_bytes; i++) out[i] = 0;
+        }
         for (int c = 0; c < d; c++) {
-          if (scale == 0.0f) {
-            out[c] = 0;
-            continue;
+          int code = 0;
+          if (scale != 0.0f) {
+            volatile float qv = row[c] / scale;
+            float r = rintf(qv); /* default rounding mode: to nearest, ties to even */
+            if (r > qmax) r = qmax;
+            if (r < -qmax) r = -qmax;
+            code = (int)r;
           }
-          volatile float qv = row[c] / scale;
-          float r = rintf(qv); /* default rounding mode: to nearest, ties to even */
-          if (r > 127.0f) r = 127.0f;
-          if (r < -127.0f) r = -127.0f;
-          out[c] = (int8_t)r;
+          if (bits == 8) {
+            out[c] = (uint8_t)(int8_t)code;
+          } else {
+            unsigned nib = (unsigned)code & 15u;
+            out[c / 2] |= (uint8_t)(c % 2 == 0 ? nib : nib << 4);
+          }
         }
       }
     }
   }
   return ORACLE_OK;
+}
+
+/* int8 cache: codes [B, Hkv, cap, d] int8, qmax 127. */
+int oracle_kv_quantize_int8(const float* x, int8_t* codes, float* scales,
+                            int B, int Hkv, int T, int d, int pos, int cap) {
+  return kv_quantize(x, (uint8_t*)codes, scales, B, Hkv, T, d, pos, cap, 127.0f, 8);
+}
+
+/* int4 cache: codes [B, Hkv, cap, d/2] bytes, qmax 7; d even. */
+int oracle_kv_quantize_int4(const float* x, uint8_t* codes, float* scales,
+                            int B, int Hkv, int T, int d, int pos, int cap) {
+  return kv_quantize(x, codes, scales, B, Hkv, T, d, pos, cap, 7.0f, 4);
 }
 
 /* Number of threads an OpenMP region will use (for reporting). */

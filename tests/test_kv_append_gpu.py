@@ -100,3 +100,26 @@ def test_full_size_append_sampled(cuda_device):
         c_ref, s_ref = oracle.kv_quantize_int8(xs)
         assert np.array_equal(codes[b, h].cpu().numpy(), c_ref[0, 0])
         assert np.array_equal(scales[b, h].cpu().numpy(), s_ref[0, 0])
+
+
+def test_kv_append_exact_ties_round_to_even(cuda_device):
+    # rows whose absmax is 127 * 2^e make the scale exactly 2^e, so (k + 1/2) * 2^e
+    # gives exact halfway quotients: each must round to the even neighbour, both signs
+    _say("case kv append exact ties")
+    d = 128
+    rows = []
+    for e in (-20, 0, 7, 60):
+        k = np.arange(-63, 64, dtype=np.float64)
+        ties = (k + 0.5) * 2.0 ** e
+        rows.append(np.concatenate([[127.0 * 2.0 ** e], ties]))
+        rows.append(np.concatenate([[-127.0 * 2.0 ** e], -ties[::-1]]))
+    x = torch.tensor(np.stack(rows), dtype=torch.float32).reshape(1, len(rows), 1, d)
+    c_ref, s_ref = oracle.kv_quantize_int8(x.numpy())
+    ties_codes = c_ref[0, 0, 0, 1:].astype(int)
+    assert np.all(ties_codes % 2 == 0)  # the oracle itself rounds every tie to even
+    codes = torch.zeros(1, 1, len(rows), d, dtype=torch.int8, device=cuda_device)
+    scales = torch.zeros(1, 1, len(rows), dtype=torch.float32, device=cuda_device)
+    fa.kv_append_int8(x.to(cuda_device), codes, scales, pos=0)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))

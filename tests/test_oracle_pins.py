@@ -418,6 +418,91 @@ def pin_quantizer_matches_torch(lib):
     assert np.array_equal(sc.transpose(0, 2, 1), s_ref.numpy())
 
 
+def _pack_int4(codes):
+    """Two signed 4-bit codes per byte: element 2i low nibble, 2i+1 high nibble."""
+    c = np.asarray(codes, dtype=np.int64)
+    return ((c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4)).astype(np.uint8)
+
+
+def _unpack_int4(packed):
+    """Inverse of _pack_int4, written with the xor form of sign extension."""
+    b = np.asarray(packed, dtype=np.int64)
+    lo, hi = ((b & 15) ^ 8) - 8, ((b >> 4) ^ 8) - 8
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int64)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    return out
+
+
+def pin_int4_decode_single_key_closed_form(lib):
+    # one cached token: every probability is 1, so O is that token's value row
+    # (code * scale, all 16 nibble values present) and lse its scaled score.
+    d = 16
+    vcodes = np.arange(-8, 8)               # every 4-bit two's complement value
+    kcodes = np.array([3, -1, 0, 7, -7, 2, -8, 5, 1, 1, -2, 4, 0, -3, 6, -5])
+    kq, vq = _pack_int4(kcodes)[None, None, None], _pack_int4(vcodes)[None, None, None]
+    assert list(vq[0, 0, 0]) == [0x98, 0xBA, 0xDC, 0xFE, 0x10, 0x32, 0x54, 0x76]
+    ks = np.full((1, 1, 1), 0.25, dtype=np.float32)
+    vs = np.full((1, 1, 1), 0.5, dtype=np.float32)
+    q = _rand((1, 2, d), 52)                # two query heads share the kv head
+    o, lse = oracle.decode_int4(q, kq, ks, vq, vs, scale=0.7, lib=lib)
+    for h in range(2):
+        assert np.array_equal(o[0, h], 0.5 * vcodes)
+        assert abs(lse[0, h] - 0.7 * float(q[0, h] @ (0.25 * kcodes))) < 1e-12
+
+
+def pin_int4_decode_equals_forward_on_dequantised(lib):
+    B, Hq, Hkv, Skv, d = 2, 6, 3, 11, 16
+    rng = np.random.default_rng(53)
+    kq = rng.integers(0, 256, (B, Hkv, Skv, d // 2), dtype=np.uint8)
+    vq = rng.integers(0, 256, (B, Hkv, Skv, d // 2), dtype=np.uint8)
+    ks = rng.uniform(0.05, 2, (B, Hkv, Skv)).astype(np.float32)
+    vs = rng.uniform(0.05, 2, (B, Hkv, Skv)).astype(np.float32)
+    q = _rand((B, Hq, d), 54)
+    o, lse = oracle.decode_int4(q, kq, ks, vq, vs, scale=0.2, lib=lib)
+    kd = _unpack_int4(kq).astype(np.float64) * ks.astype(np.float64)[..., None]
+    vd = _unpack_int4(vq).astype(np.float64) * vs.astype(np.float64)[..., None]
+    ob, lb = brute_force(q[:, None], kd.transpose(0, 2, 1, 3), vd.transpose(0, 2, 1, 3), False, 0, 0.2)
+    assert np.allclose(o, ob[:, 0], atol=1e-12, rtol=0) and np.allclose(lse, lb[:, :, 0], atol=1e-12, rtol=0)
+
+
+def pin_int4_quantizer_rounding_packing_and_bounds(lib):
+    # absmax 7 gives scale exactly 1: codes are round-half-even of the values
+    x = np.zeros((1, 1, 1, 8), dtype=np.float32)
+    x[0, 0, 0] = [7.0, 2.5, 3.5, -2.5, -3.5, 0.5, -6.5, 1.25]
+    c, sc = oracle.kv_quantize_int4(x, lib=lib)
+    assert sc[0, 0, 0] == np.float32(1.0)
+    # codes 7, 2 | 4, -2 | -4, 0 | -6, 1 packed low nibble first
+    assert list(c[0, 0, 0]) == [0x27, 0xE4, 0x0C, 0x1A]
+    rng = np.random.default_rng(55)
+    x = rng.standard_normal((2, 4, 3, 32)).astype(np.float32) * rng.uniform(0.01, 100, (2, 4, 3, 1)).astype(np.float32)
+    x[0, 3, 2] = 0.0
+    codes = np.full((2, 3, 7, 16), 0xAB, dtype=np.uint8)
+    scales = np.full((2, 3, 7), -1.0, dtype=np.float32)
+    oracle.kv_quantize_int4(x, codes, scales, pos=2, cap=7, lib=lib)
+    assert np.all(codes[:, :, :2] == 0xAB) and np.all(codes[:, :, 6:] == 0xAB)
+    assert np.all(scales[:, :, :2] == -1) and np.all(scales[:, :, 6:] == -1)
+    got_c = _unpack_int4(codes[:, :, 2:6]).transpose(0, 2, 1, 3)  # -> [B, T, Hkv, d]
+    got_s = scales[:, :, 2:6].transpose(0, 2, 1)
+    assert got_s[0, 3, 2] == 0 and np.all(got_c[0, 3, 2] == 0)
+    amax = np.abs(x).max(-1)
+    nz = amax > 0
+    assert np.all(np.abs(got_c[nz]).max(-1) == 7) and np.all(np.abs(got_c) <= 7)
+    deq = got_c * got_s[..., None].astype(np.float64)
+    assert np.all(np.abs(deq - x) <= 0.5 * got_s[..., None] * (1 + 1e-6) + 1e-30)
+    assert np.allclose(got_s[nz], amax[nz] / 7.0, rtol=1e-7, atol=0)
+
+
+def pin_int4_quantizer_matches_torch(lib):
+    import workloads as W
+    g = torch.Generator().manual_seed(56)
+    x = torch.randn(2, 9, 3, 64, generator=g) * 5
+    x[1, 4, 0] = 0
+    c_ref, s_ref = W.quantize_rows_int4(x)
+    c, sc = oracle.kv_quantize_int4(x.numpy(), lib=lib)
+    assert np.array_equal(c.transpose(0, 2, 1, 3), c_ref.numpy())
+    assert np.array_equal(sc.transpose(0, 2, 1), s_ref.numpy())
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -446,8 +531,15 @@ MUTANTS = {
                                  "const double* qrow = q + ((b * Hq + h) * Sq + i) * (int64_t)d;"),
     "top-left causal alignment": ("int64_t off = (int64_t)Skv - (int64_t)Sq;", "int64_t off = 0;"),
     "decode ignores k scale": ("double sc = (double)ks[j];", "double sc = 1.0;"),
-    "decode v uses k codes": ("const int8_t* vr = vq + j * (int64_t)d;", "const int8_t* vr = kq + j * (int64_t)d;"),
-    "quantiser step absmax/128": ("volatile float scale = amax / 127.0f;", "volatile float scale = amax / 128.0f;"),
+    "decode v uses k codes": ("const uint8_t* vr = vq + j * row_bytes;", "const uint8_t* vr = kq + j * row_bytes;"),
+    "quantiser step absmax/128": ("cap, 127.0f, 8);", "cap, 128.0f, 8);"),
+    "int4 quantiser step absmax/8": ("cap, 7.0f, 4);", "cap, 8.0f, 4);"),
+    "int4 nibbles swapped": ("(c % 2 == 0) ? (int)(row[c / 2] & 15u) : (int)(row[c / 2] >> 4);",
+                             "(c % 2 == 0) ? (int)(row[c / 2] >> 4) : (int)(row[c / 2] & 15u);"),
+    "int4 codes read unsigned": ("if (nib >= 8) nib -= 16;", "if (nib >= 16) nib -= 16;"),
+    "int4 rows strided like int8": ("const int64_t row_bytes = bits == 8 ? d : d / 2;",
+                                    "const int64_t row_bytes = d;"),
+    "int4 packing high nibble first": ("(c % 2 == 0 ? nib : nib << 4)", "(c % 2 == 0 ? nib << 4 : nib)"),
     "quantiser rounds half away from zero": ("float r = rintf(qv);", "float r = roundf(qv);"),
     "quantiser ignores the append position": ("int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;",
                                              "int64_t slot = (b * Hkv + h) * (int64_t)cap + t;"),

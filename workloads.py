@@ -14,8 +14,10 @@ round-to-nearest-even where the workload is bf16.
 The int8 cache recipe (a reading: the pages name an int8 cache with no
 scheme): symmetric per (token, kv head), scale = absmax / 127 in fp32,
 code = clamp(round_half_even(x / scale), -127, 127); an all-zero row gets
-scale 0 and codes 0.  The consumers only ever see the stored codes and
-scales, so this rounding cannot influence parity.
+scale 0 and codes 0.  The int4 cache uses the same recipe with 7 in place
+of 127 and packs two codes per byte, element 2i in the low nibble of byte i
+(signed 4-bit two's complement).  The consumers only ever see the stored
+codes and scales, so this rounding cannot influence parity.
 """
 from __future__ import annotations
 
@@ -53,6 +55,7 @@ class Decode:
     Skv: int
     d: int
     seed: int
+    bits: int = 8  # code width of the KV cache: 8 or 4
 
     @property
     def scale(self) -> float:
@@ -66,6 +69,7 @@ GQA_CAUSAL = Prefill("GQA causal prefill bf16 B1 Hq32 Hkv8 S4096 d128", 1, 32, 8
 MQA_CAUSAL = Prefill("MQA causal prefill bf16 B1 Hq232 Hkv1 S2048 d64", 1, 232, 1, 2048, 2048, 64, True, 0, "bf16", 3)
 MQA_WINDOW = Prefill("MQA causal sliding-window-512 prefill bf16 B1 Hq232 Hkv1 S2048 d64", 1, 232, 1, 2048, 2048, 64, True, 512, "bf16", 3)
 INT8_DECODE = Decode("GQA decode over int8 KV cache B32 Hq32 Hkv8 Skv32768 d128", 32, 32, 8, 32768, 128, 4)
+INT4_DECODE = Decode("GQA decode over int4 KV cache B32 Hq32 Hkv8 Skv32768 d128", 32, 32, 8, 32768, 128, 5, bits=4)
 
 PREFILL_WORKLOADS = (TINY_F32, MHA_CAUSAL, GQA_CAUSAL, MQA_CAUSAL, MQA_WINDOW)
 
@@ -108,16 +112,36 @@ def quantize_rows_int8(x: torch.Tensor):
     return codes.to(torch.int8), scale.to(torch.float32)
 
 
-def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False):
-    """q [B,Hq,d] bf16; kq/vq [B,Hkv,Skv,d] int8; k_scale/v_scale [B,Hkv,Skv] fp32.
+def quantize_rows_int4(x: torch.Tensor):
+    """Per-row symmetric int4 codes over the last axis, packed two per byte."""
+    x = x.float()
+    absmax = x.abs().amax(dim=-1)
+    scale = absmax / 7.0
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    codes = torch.round(x / safe.unsqueeze(-1)).clamp_(-7, 7)
+    codes = torch.where(scale.unsqueeze(-1) > 0, codes, torch.zeros_like(codes)).to(torch.int32)
+    nib = codes & 15
+    packed = nib[..., 0::2] | (nib[..., 1::2] << 4)
+    return packed.to(torch.uint8), scale.to(torch.float32)
+
+
+def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False, bits=8):
+    """q [B,Hq,d] bf16; kq/vq [B,Hkv,Skv,d] int8 (bits=8) or [B,Hkv,Skv,d/2]
+    uint8 holding two int4 codes per byte (bits=4); k_scale/v_scale [B,Hkv,Skv] fp32.
 
     Draw order: Q, then for each batch entry K_b [Hkv,Skv,d] and V_b, each
     quantised as soon as it is drawn (so host memory stays at one slice).
     With keep_float=True the unquantised fp32 K and V are returned as well.
     """
+    if bits not in (8, 4):
+        raise ValueError(bits)
+    quantize_rows = quantize_rows_int8 if bits == 8 else quantize_rows_int4
     g = _gen(seed, device)
     q = torch.randn((B, Hq, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
-    kq = torch.empty((B, Hkv, Skv, d), dtype=torch.int8, device=device)
+    if bits == 8:
+        kq = torch.empty((B, Hkv, Skv, d), dtype=torch.int8, device=device)
+    else:
+        kq = torch.empty((B, Hkv, Skv, d // 2), dtype=torch.uint8, device=device)
     vq = torch.empty_like(kq)
     ks = torch.empty((B, Hkv, Skv), dtype=torch.float32, device=device)
     vs = torch.empty_like(ks)
@@ -127,12 +151,12 @@ def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False):
         vf = torch.empty_like(kf)
     for b in range(B):
         kb = torch.randn((Hkv, Skv, d), generator=g, device=device, dtype=torch.float32)
-        kq[b], ks[b] = quantize_rows_int8(kb)
+        kq[b], ks[b] = quantize_rows(kb)
         if keep_float:
             kf[b] = kb
         del kb
         vb = torch.randn((Hkv, Skv, d), generator=g, device=device, dtype=torch.float32)
-        vq[b], vs[b] = quantize_rows_int8(vb)
+        vq[b], vs[b] = quantize_rows(vb)
         if keep_float:
             vf[b] = vb
         del vb
@@ -142,4 +166,4 @@ def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False):
 
 
 def decode_workload_inputs(w: Decode, device="cpu", keep_float=False):
-    return decode_inputs(w.B, w.Hq, w.Hkv, w.Skv, w.d, w.seed, device, keep_float)
+    return decode_inputs(w.B, w.Hq, w.Hkv, w.Skv, w.d, w.seed, device, keep_float, w.bits)
