@@ -35,7 +35,7 @@ METRIC = "attention TFLOP/s & % bf16 MFMA peak (prefill); HBM GB/s & % peak (dec
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak (published)
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "tiled_exact_attention_amd", "csrc", "fwd_bf16.hip")
-DECODE_KERNEL_SRC = os.path.join(ROOT, "tiled_exact_attention_amd", "csrc", "decode_int8.hip")
+DECODE_KERNEL_SRC = os.path.join(ROOT, "tiled_exact_attention_amd", "csrc", "decode_kv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 

@@ -126,6 +126,24 @@ FATTN_API int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_
                       void* stream);
 
 /*
+ * Decode over an int4 KV cache: the same operation, arguments, split plan,
+ * workspace size and error behaviour as fattn_decode_int8, with the cache
+ * compressed one step further ([FA-3MOVES] move 3 taken to 4-bit codes; the
+ * pages give no packing, this is the library's format):
+ *
+ * kq, vq     [B, Hkv, Skv, d/2] bytes: element 2i of a row is the low nibble
+ *            of byte i, element 2i+1 the high nibble, each a signed 4-bit
+ *            two's complement code (-8 .. 7; fattn_kv_append_int4 writes
+ *            -7 .. 7); the value attention sees is code * scale.
+ * k_scale, v_scale [B, Hkv, Skv] fp32, one scale per (token, kv head).
+ */
+FATTN_API int fattn_decode_int4(const void* q, const uint8_t* kq, const float* k_scale,
+                      const uint8_t* vq, const float* v_scale, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Skv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * Appends T new tokens to an int8 KV cache (the step that fills the cache
  * fattn_decode_int8 reads; [FA-3MOVES] move 3 names the int8 cache).  For each
  * (b, t, kv head) row x of d values: scale = absmax(x) / 127 in fp32 and
@@ -143,11 +161,24 @@ FATTN_API int fattn_kv_append_int8(const void* x, int8_t* codes, float* scales,
                                    int B, int T, int Hkv, int d, int pos, int cap,
                                    int dtype, void* stream);
 
-/* Number of key splits fattn_decode_int8 will use for these arguments
+/*
+ * Appends T new tokens to an int4 KV cache (the cache fattn_decode_int4
+ * reads): as fattn_kv_append_int8 with scale = absmax(x) / 7 and codes
+ * clamp(round-half-even(x_c / scale), -7, 7), packed two per byte (element
+ * 2i in the low nibble of byte i).
+ *
+ * codes  [B, Hkv, cap, d/2] bytes, scales [B, Hkv, cap] fp32.  Same argument
+ *        rules and errors as fattn_kv_append_int8.
+ */
+FATTN_API int fattn_kv_append_int4(const void* x, uint8_t* codes, float* scales,
+                                   int B, int T, int Hkv, int d, int pos, int cap,
+                                   int dtype, void* stream);
+
+/* Number of key splits fattn_decode_int8 and fattn_decode_int4 will use for these arguments
  * (>= 1), or a negative fattn_status if they are invalid.  Host only. */
 FATTN_API int fattn_decode_num_splits(int B, int Hq, int Hkv, int Skv, int d, int num_splits);
 
-/* Workspace bytes fattn_decode_int8 needs for these arguments, 0 if they are
+/* Workspace bytes fattn_decode_int8 / fattn_decode_int4 need for these arguments, 0 if they are
  * invalid.  Host only; pure function of its arguments. */
 FATTN_API size_t fattn_decode_workspace_size(int B, int Hq, int Hkv, int Skv, int d, int num_splits);
 

@@ -46,8 +46,9 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == sorted(["fattn_fwd", "fattn_decode_int8", "fattn_decode_num_splits",
-                            "fattn_decode_workspace_size", "fattn_kv_append_int8",
+    assert names == sorted(["fattn_fwd", "fattn_decode_int8", "fattn_decode_int4",
+                            "fattn_decode_num_splits", "fattn_decode_workspace_size",
+                            "fattn_kv_append_int8", "fattn_kv_append_int4",
                             "fattn_status_string", "fattn_version"])
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
@@ -138,16 +139,17 @@ def test_fwd_rejects_before_any_device_work(kw, want):
     assert _fwd(**kw) == want
 
 
-def _dec(**kw):
+def _dec(fn=None, **kw):
     a = dict(q=P, kq=P, ks=P, vq=P, vs=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Skv=100, d=128,
              scale=0.1, num_splits=0, ws=P, ws_bytes=1 << 30, stream=None)
     a.update(kw)
-    return fa.fattn_decode_int8(a["q"], a["kq"], a["ks"], a["vq"], a["vs"], a["o"], a["lse"],
-                                a["B"], a["Hq"], a["Hkv"], a["Skv"], a["d"], a["scale"],
-                                a["num_splits"], a["ws"], a["ws_bytes"], a["stream"])
+    return (fn or fa.fattn_decode_int8)(a["q"], a["kq"], a["ks"], a["vq"], a["vs"], a["o"], a["lse"],
+                                        a["B"], a["Hq"], a["Hkv"], a["Skv"], a["d"], a["scale"],
+                                        a["num_splits"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @no_gpu_only
+@pytest.mark.parametrize("fn", ["fattn_decode_int8", "fattn_decode_int4"])
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), FATTN_EINVAL), (dict(kq=None), FATTN_EINVAL), (dict(ks=None), FATTN_EINVAL),
     (dict(vq=None), FATTN_EINVAL), (dict(vs=None), FATTN_EINVAL), (dict(o=None), FATTN_EINVAL),
@@ -158,14 +160,15 @@ def _dec(**kw):
     (dict(ws=None), FATTN_EWORKSPACE), (dict(ws_bytes=16), FATTN_EWORKSPACE),
     (dict(ws=P + 8), FATTN_EWORKSPACE),
 ])
-def test_decode_rejects_before_any_device_work(kw, want):
-    assert _dec(**kw) == want
+def test_decode_rejects_before_any_device_work(fn, kw, want):
+    assert _dec(getattr(fa, fn), **kw) == want
 
 
 @no_gpu_only
-def test_decode_workspace_boundary_is_exact():
+@pytest.mark.parametrize("fn", ["fattn_decode_int8", "fattn_decode_int4"])
+def test_decode_workspace_boundary_is_exact(fn):
     need = fa.decode_workspace_size(1, 4, 2, 100, 128, 0)
-    assert _dec(ws_bytes=need - 1) == FATTN_EWORKSPACE
+    assert _dec(getattr(fa, fn), ws_bytes=need - 1) == FATTN_EWORKSPACE
 
 
 def test_torch_wrappers_reject_cpu_tensors():
@@ -177,19 +180,29 @@ def test_torch_wrappers_reject_cpu_tensors():
         fa.fwd(q.half(), q.half(), q.half())
 
 
-def _app(**kw):
+def _app(fn=None, **kw):
     a = dict(x=P, codes=P, scales=P, B=1, T=4, Hkv=2, d=128, pos=0, cap=8, dtype=1, stream=None)
     a.update(kw)
-    return fa.fattn_kv_append_int8(a["x"], a["codes"], a["scales"], a["B"], a["T"], a["Hkv"], a["d"],
-                                   a["pos"], a["cap"], a["dtype"], a["stream"])
+    return (fn or fa.fattn_kv_append_int8)(a["x"], a["codes"], a["scales"], a["B"], a["T"], a["Hkv"],
+                                           a["d"], a["pos"], a["cap"], a["dtype"], a["stream"])
 
 
 @no_gpu_only
+@pytest.mark.parametrize("fn", ["fattn_kv_append_int8", "fattn_kv_append_int4"])
 @pytest.mark.parametrize("kw,want", [
     (dict(x=None), FATTN_EINVAL), (dict(codes=None), FATTN_EINVAL), (dict(scales=None), FATTN_EINVAL),
     (dict(scales=P + 4), FATTN_EINVAL), (dict(B=0), FATTN_EINVAL), (dict(T=0), FATTN_EINVAL),
     (dict(pos=-1), FATTN_EINVAL), (dict(pos=5), FATTN_EINVAL), (dict(T=9), FATTN_EINVAL),
     (dict(d=96), FATTN_EUNSUPPORTED), (dict(dtype=3), FATTN_EUNSUPPORTED),
 ])
-def test_kv_append_rejects_before_any_device_work(kw, want):
-    assert _app(**kw) == want
+def test_kv_append_rejects_before_any_device_work(fn, kw, want):
+    assert _app(getattr(fa, fn), **kw) == want
+
+
+def test_int4_wrappers_check_the_packed_shape():
+    import torch
+    q = torch.zeros(1, 4, 64, dtype=torch.bfloat16)
+    kq = torch.zeros(1, 2, 10, 64, dtype=torch.uint8)  # unpacked width: wrong for int4
+    s = torch.zeros(1, 2, 10)
+    with pytest.raises(ValueError):
+        fa.decode_int4(q, kq, s, kq, s)  # CPU tensors are rejected before any shape use

@@ -1,11 +1,13 @@
 """ctypes marshalling for libfattn (argument checks and pointers only).
 
-The raw entry points ``fattn_fwd``, ``fattn_decode_int8``,
+The raw entry points (``fattn_fwd``, ``fattn_decode_int8``,
+``fattn_decode_int4``, ``fattn_kv_append_int8``, ``fattn_kv_append_int4``,
 ``fattn_decode_workspace_size``, ``fattn_decode_num_splits``,
-``fattn_status_string`` and ``fattn_version`` have the C names and take plain
-integers (device pointers as ints, streams as ints or None).  ``fwd`` and
-``decode_int8`` accept torch tensors, allocate the outputs and call them on
-the current torch stream of the tensors' device.
+``fattn_status_string``, ``fattn_version``) have the C names and take plain
+integers (device pointers as ints, streams as ints or None).  ``fwd``,
+``decode_int8``, ``decode_int4``, ``kv_append_int8`` and ``kv_append_int4``
+accept torch tensors, allocate the outputs and call them on the current torch
+stream of the tensors' device.
 """
 from __future__ import annotations
 
@@ -49,8 +51,12 @@ def load():
         lib.fattn_decode_int8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                           f32, i32, vp, sz, vp]
         lib.fattn_decode_int8.restype = i32
+        lib.fattn_decode_int4.argtypes = lib.fattn_decode_int8.argtypes
+        lib.fattn_decode_int4.restype = i32
         lib.fattn_kv_append_int8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         lib.fattn_kv_append_int8.restype = i32
+        lib.fattn_kv_append_int4.argtypes = lib.fattn_kv_append_int8.argtypes
+        lib.fattn_kv_append_int4.restype = i32
         lib.fattn_decode_num_splits.argtypes = [i32] * 6
         lib.fattn_decode_num_splits.restype = i32
         lib.fattn_decode_workspace_size.argtypes = [i32] * 6
@@ -76,8 +82,18 @@ def fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, s
                                     scale, num_splits, workspace, workspace_bytes, stream)
 
 
+def fattn_decode_int4(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
+                      num_splits, workspace, workspace_bytes, stream) -> int:
+    return load().fattn_decode_int4(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d,
+                                    scale, num_splits, workspace, workspace_bytes, stream)
+
+
 def fattn_kv_append_int8(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream) -> int:
     return load().fattn_kv_append_int8(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream)
+
+
+def fattn_kv_append_int4(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream) -> int:
+    return load().fattn_kv_append_int4(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream)
 
 
 def fattn_decode_num_splits(B, Hq, Hkv, Skv, d, num_splits) -> int:
@@ -170,24 +186,18 @@ def decode_workspace_size(B, Hq, Hkv, Skv, d, num_splits=0) -> int:
     return n
 
 
-def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_splits: int = 0,
-                workspace=None, return_lse: bool = False, out=None):
-    """Decode attention of one token over an int8 KV cache (see fattn_decode_int8).
-
-    q [B, Hq, d] bf16; kq/vq [B, Hkv, Skv, d] int8; k_scale/v_scale [B, Hkv, Skv] fp32.
-    workspace: optional uint8 GPU tensor of at least decode_workspace_size(...)
-    bytes (allocated here if None).  Returns o [B, Hq, d] bf16 (and lse [B, Hq]).
-    """
+def _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, bits):
     import torch
     _check(q, "q", torch.bfloat16, 3)
     dev = q.device
-    _check(kq, "kq", torch.int8, 4, dev)
-    _check(vq, "vq", torch.int8, 4, dev)
+    code_t = torch.int8 if bits == 8 else torch.uint8
+    _check(kq, "kq", code_t, 4, dev)
+    _check(vq, "vq", code_t, 4, dev)
     _check(k_scale, "k_scale", torch.float32, 3, dev)
     _check(v_scale, "v_scale", torch.float32, 3, dev)
     B, Hq, d = q.shape
-    Bk, Hkv, Skv, dk = kq.shape
-    if Bk != B or dk != d or tuple(vq.shape) != tuple(kq.shape):
+    Bk, Hkv, Skv, rb = kq.shape
+    if Bk != B or rb * (8 // bits) != d or tuple(vq.shape) != tuple(kq.shape):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kq {tuple(kq.shape)}, vq {tuple(vq.shape)}")
     if tuple(k_scale.shape) != (B, Hkv, Skv) or tuple(v_scale.shape) != (B, Hkv, Skv):
         raise ValueError("k_scale and v_scale must be [B, Hkv, Skv]")
@@ -206,35 +216,67 @@ def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
+    fn, name = (fattn_decode_int8, "fattn_decode_int8") if bits == 8 else (fattn_decode_int4, "fattn_decode_int4")
     with torch.cuda.device(dev):
-        st = fattn_decode_int8(q.data_ptr(), kq.data_ptr(), k_scale.data_ptr(), vq.data_ptr(),
-                               v_scale.data_ptr(), out.data_ptr(),
-                               lse.data_ptr() if lse is not None else None,
-                               B, Hq, Hkv, Skv, d, float(scale), int(num_splits),
-                               workspace.data_ptr(), ws_bytes, _stream_of(dev))
+        st = fn(q.data_ptr(), kq.data_ptr(), k_scale.data_ptr(), vq.data_ptr(),
+                v_scale.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                B, Hq, Hkv, Skv, d, float(scale), int(num_splits),
+                workspace.data_ptr(), ws_bytes, _stream_of(dev))
     if st != 0:
-        raise FattnError(st, "fattn_decode_int8")
+        raise FattnError(st, name)
     return (out, lse) if return_lse else out
+
+
+def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_splits: int = 0,
+                workspace=None, return_lse: bool = False, out=None):
+    """Decode attention of one token over an int8 KV cache (see fattn_decode_int8).
+
+    q [B, Hq, d] bf16; kq/vq [B, Hkv, Skv, d] int8; k_scale/v_scale [B, Hkv, Skv] fp32.
+    workspace: optional uint8 GPU tensor of at least decode_workspace_size(...)
+    bytes (allocated here if None).  Returns o [B, Hq, d] bf16 (and lse [B, Hq]).
+    """
+    return _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, 8)
+
+
+def decode_int4(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_splits: int = 0,
+                workspace=None, return_lse: bool = False, out=None):
+    """Decode attention of one token over an int4 KV cache (see fattn_decode_int4).
+
+    As decode_int8, with kq/vq [B, Hkv, Skv, d/2] uint8 holding two signed
+    4-bit codes per byte (element 2i in the low nibble of byte i).
+    """
+    return _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, 4)
+
+
+def _kv_append(x, codes, scales, pos, bits):
+    import torch
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _check(x, "x", x.dtype, 4)
+    _check(codes, "codes", torch.int8 if bits == 8 else torch.uint8, 4, x.device)
+    _check(scales, "scales", torch.float32, 3, x.device)
+    B, T, Hkv, d = x.shape
+    Bc, Hc, cap, rb = codes.shape
+    if (Bc, Hc, rb * (8 // bits)) != (B, Hkv, d) or tuple(scales.shape) != (B, Hkv, cap):
+        raise ValueError(f"cache shapes {tuple(codes.shape)}, {tuple(scales.shape)} do not match x {tuple(x.shape)}")
+    fn, name = (fattn_kv_append_int8, "fattn_kv_append_int8") if bits == 8 else \
+        (fattn_kv_append_int4, "fattn_kv_append_int4")
+    with torch.cuda.device(x.device):
+        st = fn(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, T, Hkv, d, int(pos), cap,
+                FATTN_F32 if x.dtype == torch.float32 else FATTN_BF16, _stream_of(x.device))
+    if st != 0:
+        raise FattnError(st, name)
+    return codes, scales
 
 
 def kv_append_int8(x, codes, scales, *, pos: int):
     """Quantise new tokens x [B, T, Hkv, d] (float32 or bfloat16) into the int8
     cache codes [B, Hkv, cap, d] / scales [B, Hkv, cap] at positions pos .. pos+T-1
     (see fattn_kv_append_int8).  Updates codes and scales in place and returns them."""
-    import torch
-    if x.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("x must be float32 or bfloat16")
-    _check(x, "x", x.dtype, 4)
-    _check(codes, "codes", torch.int8, 4, x.device)
-    _check(scales, "scales", torch.float32, 3, x.device)
-    B, T, Hkv, d = x.shape
-    Bc, Hc, cap, dc = codes.shape
-    if (Bc, Hc, dc) != (B, Hkv, d) or tuple(scales.shape) != (B, Hkv, cap):
-        raise ValueError(f"cache shapes {tuple(codes.shape)}, {tuple(scales.shape)} do not match x {tuple(x.shape)}")
-    with torch.cuda.device(x.device):
-        st = fattn_kv_append_int8(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), B, T, Hkv, d,
-                                  int(pos), cap, FATTN_F32 if x.dtype == torch.float32 else FATTN_BF16,
-                                  _stream_of(x.device))
-    if st != 0:
-        raise FattnError(st, "fattn_kv_append_int8")
-    return codes, scales
+    return _kv_append(x, codes, scales, pos, 8)
+
+
+def kv_append_int4(x, codes, scales, *, pos: int):
+    """As kv_append_int8 for the int4 cache: codes [B, Hkv, cap, d/2] uint8
+    (see fattn_kv_append_int4)."""
+    return _kv_append(x, codes, scales, pos, 4)

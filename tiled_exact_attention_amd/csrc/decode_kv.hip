@@ -1,10 +1,11 @@
-// Split-KV decode over an int8 KV cache, then a log-sum-exp merge.
+// Split-KV decode over an int8 or int4 KV cache, then a log-sum-exp merge.
 //
 // Method: one query token per sequence attends to all cached tokens.  The
-// cache keeps int8 codes with an fp32 scale per (token, kv head) and is used
+// cache keeps int8 codes (or int4 codes, two per byte, element 2i in the low
+// nibble of byte i) with an fp32 scale per (token, kv head) and is used
 // without a decompressed copy ([FA-3MOVES] move 3): codes are converted to
-// bf16 in registers (exact, |code| <= 127) and the scales are applied to the
-// scores (k scale) and to the probabilities (v scale).  The keys of each
+// bf16 in registers (exact) and the scales are applied to the scores (k
+// scale) and to the probabilities (v scale).  The keys of each
 // (batch, kv head) stream are cut into splits; each split runs the online
 // softmax of the [FA-NPU] tiling section over its tokens and writes a
 // normalised partial output and its log-sum-exp; a second kernel merges the
@@ -24,9 +25,18 @@
 //    ds_read_b64_tr_b8 in exactly the token order of the P^T registers; the
 //    codes become the A operand of O^T += V^T P^T.
 //  * loads run three tiles ahead of use through a four-slot register ring
-//    (about 25 KB in flight per wave), which is what keeps HBM busy: the
-//    kernel is bound by bytes in flight, not by arithmetic.  Scales arrive as
-//    one dword per lane per tile and are redistributed through LDS.
+//    (about 25 KB in flight per wave with int8 codes), which is what keeps
+//    HBM busy: the kernel is bound by bytes in flight, not by arithmetic.
+//    Scales arrive as one dword per lane per tile and are redistributed
+//    through LDS.
+//  * int4 codes: a nibble moved into the high half of a byte is the int8
+//    value 16*code, so the int8 conversion serves both widths and the factor
+//    16 (a power of two, exact) is taken out of the score constant and the
+//    final normalisation.  For K each lane group holds d/4 contiguous dims of
+//    its token; a k-step takes one dword (8 dims) in the order even dims,
+//    then odd dims, and the query operand is permuted the same way.  For V
+//    one transposed read yields both nibbles of a byte column: the low
+//    nibbles (even dims) and the high nibbles (odd dims) feed two products.
 #include "device_util.h"
 #include "launch.h"
 
@@ -48,9 +58,9 @@ static_assert(kDecodeTile % kTile == 0, "split chunks must hold whole tiles");
 
 struct SplitParams {
   const __bf16* q;
-  const int8_t* kq;
+  const uint8_t* kq;
   const float* ks;
-  const int8_t* vq;
+  const uint8_t* vq;
   const float* vs;
   float* part_o;
   float* part_lse;
@@ -59,26 +69,59 @@ struct SplitParams {
   int nhc;      // head chunks per kv head: ceil(G / 16)
   int nsplit;
   int chunk;    // tokens per split
-  float c;      // scale * log2(e)
+  float c;      // scale * log2(e) (divided by 16 for int4 codes)
 };
+
+// Byte counts of one tile for a code width.
+template <int D, int BITS>
+struct Geom {
+  static constexpr int RB = D * BITS / 8;         // bytes per token row
+  static constexpr int KB = RB / 4;               // K bytes per lane per token (a quarter row)
+  static constexpr int KW = KB / 4;               // ... in dwords
+  static constexpr int CPR = RB / 16;             // 16-byte pieces per V row
+  static constexpr int RPL = 64 / CPR;            // V rows per load instruction
+  static constexpr int VLOADS = kTile / RPL;      // 16-byte V loads per lane per tile
+  static constexpr int VSTRIDE = RB + 16;         // padded LDS row (bytes)
+  static constexpr int NREAD = RB / 16;           // transposed V reads per tile
+};
+
+// KB bytes at src as dwords w[0 .. KB/4) (zero when !ok: past the split end).
+template <int KB>
+__device__ __forceinline__ void load_k(const uint8_t* src, bool ok, uint32_t* w) {
+  if constexpr (KB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < KB / 16; ++i) {
+      const uint4 x = ok ? reinterpret_cast<const uint4*>(src)[i] : make_uint4(0u, 0u, 0u, 0u);
+      w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+    }
+  } else {
+    static_assert(KB == 8, "a quarter row is 8, 16 or 32 bytes");
+    const uint2 x = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
+    w[0] = x.x; w[1] = x.y;
+  }
+}
 
 // Loads of one 32-token tile held in registers between issue and use.
-template <int D>
+template <int D, int BITS>
 struct TileRegs {
-  uint4 k[2][D / 64];   // K codes, MFMA A layout: token 16*blk + l%16, dims 16*(l/16 + 4u) ..
-  uint4 v[D / 32];      // V codes, coalesced: 64 lanes x 16 bytes per load
-  float sc;             // lane l < 32: k scale of token l; lane l >= 32: v scale of token l - 32
+  // K codes in the MFMA A layout: token 16*blk + l%16, a quarter row per lane
+  // group (int8: 16-byte pieces g + 4u; int4: contiguous bytes KB*g ..)
+  uint32_t k[2][Geom<D, BITS>::KW];
+  uint4 v[Geom<D, BITS>::VLOADS];  // V codes, coalesced: 64 lanes x 16 bytes per load
+  float sc;  // lane l < 32: k scale of token l; lane l >= 32: v scale of token l - 32
 };
 
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
-  constexpr int KU = D / 64;              // 16-byte K pieces per token per lane group
-  constexpr int KM = D / 32;              // k-steps of the QK product (32 dims each)
-  constexpr int VLOADS = D / 32;          // 16-byte V loads per lane per tile
-  constexpr int CPR = D / 16;             // 16-byte pieces per V row
-  constexpr int RPL = 64 / CPR;           // V rows per load instruction
-  constexpr int VSTRIDE = D + 16;         // padded LDS row (bytes)
-  constexpr int CB = D / 16;              // 16-dim blocks of the output
+  using GM = Geom<D, BITS>;
+  constexpr int RB = GM::RB;
+  constexpr int KB = GM::KB;
+  constexpr int KM = D / 32;              // k-steps of the QK product (8 dims per lane each)
+  constexpr int VLOADS = GM::VLOADS;
+  constexpr int CPR = GM::CPR;
+  constexpr int RPL = GM::RPL;
+  constexpr int VSTRIDE = GM::VSTRIDE;
+  constexpr int CB = D / 16;              // 16-dim blocks of the output (= products per tile)
   __shared__ __attribute__((aligned(16))) char vlds[kTile * VSTRIDE];
   __shared__ __attribute__((aligned(16))) float slds[2 * kTile];   // k scales, then v scales
 
@@ -97,8 +140,8 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   const bool head_ok = n < nheads;
 
   const int64_t stream = int64_t(b) * p.Hkv + hk;
-  const int8_t* kbase = p.kq + stream * p.Skv * D;
-  const int8_t* vbase = p.vq + stream * p.Skv * D;
+  const uint8_t* kbase = p.kq + stream * p.Skv * RB;
+  const uint8_t* vbase = p.vq + stream * p.Skv * RB;
   const float* ksb = p.ks + stream * p.Skv;
   const float* vsb = p.vs + stream * p.Skv;
 
@@ -106,16 +149,23 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   const int t_end = min(p.Skv, t_begin + p.chunk);
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
-  // query heads as the B operand: k-step m covers dims 16*(g + 4*(m/2)) + 8*(m%2) .. +7
+  // query heads as the B operand.  k-step m covers, for lane group g,
+  //   int8: dims 16*(g + 4*(m/2)) + 8*(m%2) .. +7 in order
+  //   int4: dims (d/4)*g + 8m + {0, 2, 4, 6, 1, 3, 5, 7}
   bf16x8 qf[KM];
   {
     const __bf16* qrow = p.q + (int64_t(b) * p.Hq + (head_ok ? hq : hk * p.G)) * D;
 #pragma unroll
     for (int m = 0; m < KM; ++m) {
-      const int d0 = 16 * (g + 4 * (m >> 1)) + 8 * (m & 1);
+      const int d0 = BITS == 8 ? 16 * (g + 4 * (m >> 1)) + 8 * (m & 1) : (D / 4) * g + 8 * m;
       uint4 raw = *reinterpret_cast<const uint4*>(qrow + d0);
       if (!head_ok) raw = make_uint4(0u, 0u, 0u, 0u);
-      qf[m] = __builtin_bit_cast(bf16x8, raw);
+      const bf16x8 x = __builtin_bit_cast(bf16x8, raw);
+      if constexpr (BITS == 8) {
+        qf[m] = x;
+      } else {
+        qf[m] = __builtin_shufflevector(x, x, 0, 2, 4, 6, 1, 3, 5, 7);
+      }
     }
   }
 
@@ -124,22 +174,23 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   const int v_row = lane / CPR, v_col = 16 * (lane % CPR);
   const float* sc_src = lane < kTile ? ksb : vsb;
   const int sc_tok = lane & (kTile - 1);
-  auto load_tile = [&](int t, TileRegs<D>& r) __attribute__((always_inline)) {
+  auto load_tile = [&](int t, TileRegs<D, BITS>& r) __attribute__((always_inline)) {
     const int t0 = t_begin + t * kTile;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int tok = t0 + 16 * blk + n;
+      const uint8_t* krow = kbase + int64_t(tok) * RB;
+      if constexpr (BITS == 8) {
 #pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        r.k[blk][u] = tok < t_end
-            ? *reinterpret_cast<const uint4*>(kbase + int64_t(tok) * D + 16 * (g + 4 * u))
-            : make_uint4(0u, 0u, 0u, 0u);
+        for (int u = 0; u < KB / 16; ++u) load_k<16>(krow + 16 * (g + 4 * u), tok < t_end, &r.k[blk][4 * u]);
+      } else {
+        load_k<KB>(krow + KB * g, tok < t_end, r.k[blk]);
       }
     }
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int tok = t0 + i * RPL + v_row;
-      r.v[i] = tok < t_end ? *reinterpret_cast<const uint4*>(vbase + int64_t(tok) * D + v_col)
+      r.v[i] = tok < t_end ? *reinterpret_cast<const uint4*>(vbase + int64_t(tok) * RB + v_col)
                            : make_uint4(0u, 0u, 0u, 0u);
     }
     const int stok = t0 + sc_tok;
@@ -158,7 +209,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   const int vrow = e_src < 4 ? 4 * g + e_src : 16 + 4 * g + (e_src - 4);
   const char* vread = vlds + vrow * VSTRIDE + 8 * (s16 & 1);
 
-  auto process = [&](int t, const TileRegs<D>& r) __attribute__((always_inline)) {
+  auto process = [&](int t, const TileRegs<D, BITS>& r) __attribute__((always_inline)) {
     const int t0 = t_begin + t * kTile;
     // stage V codes (row-major, padded rows) and the tile's scales
 #pragma unroll
@@ -174,8 +225,13 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
       s[blk] = f32x4{};
 #pragma unroll
       for (int m = 0; m < KM; ++m) {
-        const uint4 w = r.k[blk][m >> 1];
-        const bf16x8 a = (m & 1) ? i8x8_to_bf16x8(w.z, w.w) : i8x8_to_bf16x8(w.x, w.y);
+        bf16x8 a;
+        if constexpr (BITS == 8) {
+          a = i8x8_to_bf16x8(r.k[blk][2 * m], r.k[blk][2 * m + 1]);
+        } else {  // 16 * code: even dims of the dword, then odd dims
+          const uint32_t w = r.k[blk][m];
+          a = i8x8_to_bf16x8((w << 4) & 0xf0f0f0f0u, w & 0xf0f0f0f0u);
+        }
         s[blk] = mfma16(a, qf[m], s[blk]);
       }
     }
@@ -222,15 +278,22 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
 
     // O^T += V^T P^T with V^T read transposed from the staged tile
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
+    for (int cb = 0; cb < GM::NREAD; ++cb) {
       const i32x2 raw = lds_read_tr8(vread + 16 * cb);
-      const bf16x8 a = i8x8_to_bf16x8(uint32_t(raw[0]), uint32_t(raw[1]));
-      acc[cb] = mfma16(a, pf, acc[cb]);
+      const uint32_t r0w = uint32_t(raw[0]), r1w = uint32_t(raw[1]);
+      if constexpr (BITS == 8) {
+        acc[cb] = mfma16(i8x8_to_bf16x8(r0w, r1w), pf, acc[cb]);
+      } else {  // byte column 16cb + t: even dim from the low nibbles, odd from the high
+        acc[2 * cb] = mfma16(i8x8_to_bf16x8((r0w << 4) & 0xf0f0f0f0u, (r1w << 4) & 0xf0f0f0f0u),
+                             pf, acc[2 * cb]);
+        acc[2 * cb + 1] = mfma16(i8x8_to_bf16x8(r0w & 0xf0f0f0f0u, r1w & 0xf0f0f0f0u), pf,
+                                 acc[2 * cb + 1]);
+      }
     }
   };
 
   // four-slot register ring: tiles t+1 .. t+3 are in flight while t is processed
-  TileRegs<D> r0, r1, r2, r3;
+  TileRegs<D, BITS> r0, r1, r2, r3;
   if (0 < ntiles) load_tile(0, r0);
   if (1 < ntiles) load_tile(1, r1);
   if (2 < ntiles) load_tile(2, r2);
@@ -252,13 +315,24 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (!head_ok) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  // int4 values entered as 16 * code: the factor leaves with the normalisation
+  const float inv = l_tot > 0.f ? (BITS == 8 ? 1.f : 0.0625f) / l_tot : 0.f;
   const int64_t prow = (int64_t(b) * p.Hq + hq) * p.nsplit + split;
   float* po = p.part_o + prow * D;
+  if constexpr (BITS == 8) {
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    // acc[cb][r] holds output dim 16*cb + 4g + r of head slot n
-    *reinterpret_cast<f32x4*>(po + 16 * cb + 4 * g) = acc[cb] * inv;
+    for (int cb = 0; cb < CB; ++cb) {
+      // acc[cb][r] holds output dim 16*cb + 4g + r of head slot n
+      *reinterpret_cast<f32x4*>(po + 16 * cb + 4 * g) = acc[cb] * inv;
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < GM::NREAD; ++cb) {
+      // acc[2cb][r] / acc[2cb+1][r]: dims 32*cb + 8g + 2r and that + 1
+      const f32x4 e = acc[2 * cb] * inv, o = acc[2 * cb + 1] * inv;
+      *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
+      *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
+    }
   }
   if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
 }
@@ -296,14 +370,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
   if (lse && lane == 0) lse[row] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
+template <int D, int BITS>
+void launch_split_and_merge(const DecodeArgs& a, const SplitParams& p, unsigned waves,
+                            unsigned rows, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<D, BITS>), dim3(waves), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(rows), dim3(64), 0, stream,
+                     a.part_o, a.part_lse, static_cast<__bf16*>(a.o), a.lse, a.nsplit);
+}
+
 }  // namespace
 
-hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   SplitParams p;
   p.q = static_cast<const __bf16*>(a.q);
-  p.kq = a.kq;
+  p.kq = static_cast<const uint8_t*>(a.kq);
   p.ks = a.kscale;
-  p.vq = a.vq;
+  p.vq = static_cast<const uint8_t*>(a.vq);
   p.vs = a.vscale;
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
@@ -314,18 +396,18 @@ hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream) {
   p.nhc = (p.G + kHeadsPerWave - 1) / kHeadsPerWave;
   p.nsplit = a.nsplit;
   p.chunk = a.chunk;
-  p.c = a.scale * 1.4426950408889634f;
+  p.c = a.scale * 1.4426950408889634f * (a.bits == 8 ? 1.f : 0.0625f);
   const int64_t waves = int64_t(a.B) * a.Hkv * p.nhc * a.nsplit;
   const int64_t rows = int64_t(a.B) * a.Hq;
   if (waves > 0x7fffffff || rows > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.bits != 8 && a.bits != 4) return hipErrorInvalidValue;
+  const unsigned w = unsigned(waves), r = unsigned(rows);
   if (a.d == 64) {
-    hipLaunchKernelGGL(decode_split_kernel<64>, dim3(unsigned(waves)), dim3(64), 0, stream, p);
-    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3(unsigned(rows)), dim3(64), 0, stream,
-                       a.part_o, a.part_lse, static_cast<__bf16*>(a.o), a.lse, a.nsplit);
+    if (a.bits == 8) launch_split_and_merge<64, 8>(a, p, w, r, stream);
+    else launch_split_and_merge<64, 4>(a, p, w, r, stream);
   } else {
-    hipLaunchKernelGGL(decode_split_kernel<128>, dim3(unsigned(waves)), dim3(64), 0, stream, p);
-    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3(unsigned(rows)), dim3(64), 0, stream,
-                       a.part_o, a.part_lse, static_cast<__bf16*>(a.o), a.lse, a.nsplit);
+    if (a.bits == 8) launch_split_and_merge<128, 8>(a, p, w, r, stream);
+    else launch_split_and_merge<128, 4>(a, p, w, r, stream);
   }
   return hipGetLastError();
 }

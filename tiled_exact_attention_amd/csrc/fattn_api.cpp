@@ -88,6 +88,43 @@ size_t workspace_bytes_for(int B, int Hq, int nsplit, int d) {
   return o_bytes + rows * sizeof(float);
 }
 
+int decode(const void* q, const void* kq, const float* k_scale, const void* vq,
+           const float* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Skv, int d,
+           float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream,
+           int bits) {
+  int st = validate_decode(q, kq, k_scale, vq, v_scale, o, B, Hq, Hkv, Skv, d, scale,
+                           num_splits, true);
+  if (st != FATTN_OK) return st;
+  int nsplit, chunk;
+  plan_splits(B, Hq, Hkv, Skv, num_splits, &nsplit, &chunk);
+  size_t need = workspace_bytes_for(B, Hq, nsplit, d);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FATTN_EWORKSPACE;
+  if (lse && !aligned16(lse)) return FATTN_EINVAL;
+
+  size_t rows = size_t(B) * size_t(Hq) * size_t(nsplit);
+  size_t o_bytes = (rows * size_t(d) * sizeof(float) + 255) / 256 * 256;
+  fattn::DecodeArgs a{q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
+                      nsplit, chunk, static_cast<float*>(workspace),
+                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes), bits};
+  hipError_t err = fattn::launch_decode(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+}
+
+int kv_append(const void* x, void* codes, float* scales, int B, int T, int Hkv, int d, int pos,
+              int cap, int dtype, void* stream, int bits) {
+  if (!x || !codes || !scales) return FATTN_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FATTN_EINVAL;
+  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || pos < 0 || cap < 1) return FATTN_EINVAL;
+  if (int64_t(pos) + T > cap) return FATTN_EINVAL;
+  if (!fits(B, T, Hkv, d) || !fits(B, Hkv, cap, d)) return FATTN_EINVAL;
+  if (int64_t(B) * T * Hkv > int64_t(0x7fffffff) * 16) return FATTN_EINVAL;
+  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
+  if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
+  fattn::KvQuantArgs a{x, codes, scales, B, T, Hkv, d, pos, cap, dtype == FATTN_BF16, bits};
+  hipError_t err = fattn::launch_kv_quant(a, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,37 +171,27 @@ int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_scale,
                       int B, int Hq, int Hkv, int Skv, int d, float scale,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  int st = validate_decode(q, kq, k_scale, vq, v_scale, o, B, Hq, Hkv, Skv, d, scale,
-                           num_splits, true);
-  if (st != FATTN_OK) return st;
-  int nsplit, chunk;
-  plan_splits(B, Hq, Hkv, Skv, num_splits, &nsplit, &chunk);
-  size_t need = workspace_bytes_for(B, Hq, nsplit, d);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FATTN_EWORKSPACE;
-  if (lse && !aligned16(lse)) return FATTN_EINVAL;
+  return decode(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits,
+                workspace, workspace_bytes, stream, 8);
+}
 
-  size_t rows = size_t(B) * size_t(Hq) * size_t(nsplit);
-  size_t o_bytes = (rows * size_t(d) * sizeof(float) + 255) / 256 * 256;
-  fattn::DecodeArgs a{q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
-                      nsplit, chunk, static_cast<float*>(workspace),
-                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes)};
-  hipError_t err = fattn::launch_decode_int8(a, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+int fattn_decode_int4(const void* q, const uint8_t* kq, const float* k_scale,
+                      const uint8_t* vq, const float* v_scale, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Skv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits,
+                workspace, workspace_bytes, stream, 4);
 }
 
 int fattn_kv_append_int8(const void* x, int8_t* codes, float* scales,
                          int B, int T, int Hkv, int d, int pos, int cap, int dtype, void* stream) {
-  if (!x || !codes || !scales) return FATTN_EINVAL;
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return FATTN_EINVAL;
-  if (B < 1 || T < 1 || Hkv < 1 || d < 1 || pos < 0 || cap < 1) return FATTN_EINVAL;
-  if (int64_t(pos) + T > cap) return FATTN_EINVAL;
-  if (!fits(B, T, Hkv, d) || !fits(B, Hkv, cap, d)) return FATTN_EINVAL;
-  if (int64_t(B) * T * Hkv > int64_t(0x7fffffff) * 16) return FATTN_EINVAL;
-  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
-  if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
-  fattn::KvQuantArgs a{x, codes, scales, B, T, Hkv, d, pos, cap, dtype == FATTN_BF16};
-  hipError_t err = fattn::launch_kv_quant(a, static_cast<hipStream_t>(stream));
-  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+  return kv_append(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream, 8);
+}
+
+int fattn_kv_append_int4(const void* x, uint8_t* codes, float* scales,
+                         int B, int T, int Hkv, int d, int pos, int cap, int dtype, void* stream) {
+  return kv_append(x, codes, scales, B, T, Hkv, d, pos, cap, dtype, stream, 4);
 }
 
 const char* fattn_status_string(int status) {

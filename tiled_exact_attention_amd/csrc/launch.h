@@ -21,12 +21,12 @@ struct FwdArgs {
   int window;
 };
 
-// Arguments of one int8-cache decode call after validation and split planning.
+// Arguments of one quantised-cache decode call after validation and split planning.
 struct DecodeArgs {
   const void* q;          // [B, Hq, d] bf16
-  const int8_t* kq;       // [B, Hkv, Skv, d]
+  const void* kq;         // [B, Hkv, Skv, d * bits / 8] codes
   const float* kscale;    // [B, Hkv, Skv]
-  const int8_t* vq;
+  const void* vq;
   const float* vscale;
   void* o;                // [B, Hq, d] bf16
   float* lse;             // [B, Hq] or null
@@ -36,20 +36,22 @@ struct DecodeArgs {
   int chunk;              // tokens per split (a multiple of the kernel's key tile)
   float* part_o;          // workspace: [B, Hq, nsplit, d] fp32
   float* part_lse;        // workspace: [B, Hq, nsplit] fp32
+  int bits;               // code width: 8 (int8) or 4 (two int4 codes per byte)
 };
 
-// Arguments of one int8 KV-cache append after validation.
+// Arguments of one KV-cache append after validation.
 struct KvQuantArgs {
   const void* x;          // [B, T, Hkv, d] bf16 or fp32
-  int8_t* codes;          // [B, Hkv, cap, d]
+  void* codes;            // [B, Hkv, cap, d * bits / 8]
   float* scales;          // [B, Hkv, cap]
   int B, T, Hkv, d, pos, cap;
   bool bf16;
+  int bits;               // 8: int8 codes, scale absmax/127; 4: packed int4, absmax/7
 };
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_decode_int8(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_quant(const KvQuantArgs& a, hipStream_t stream);
 
 // Key-tile length of the decode split kernel; split chunks are multiples of it.
