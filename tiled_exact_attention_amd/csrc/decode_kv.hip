@@ -29,14 +29,18 @@
 //    HBM busy: the kernel is bound by bytes in flight, not by arithmetic.
 //    Scales arrive as one dword per lane per tile and are redistributed
 //    through LDS.
-//  * int4 codes: a nibble moved into the high half of a byte is the int8
-//    value 16*code, so the int8 conversion serves both widths and the factor
-//    16 (a power of two, exact) is taken out of the score constant and the
-//    final normalisation.  For K each lane group holds d/4 contiguous dims of
-//    its token; a k-step takes one dword (8 dims) in the order even dims,
-//    then odd dims, and the query operand is permuted the same way.  For V
-//    one transposed read yields both nibbles of a byte column: the low
-//    nibbles (even dims) and the high nibbles (odd dims) feed two products.
+//  * int4 codes: code + 8 (0 .. 15) placed in the low byte under a 0x43 high
+//    byte is the bf16 bit pattern of 136 + code, exact, built with one byte
+//    permute per two values.  The products then carry a bias: for the scores
+//    it is 136 * sum(q) per query head, computed once with the same products
+//    and subtracted; for the output it is 136 * sum(p') over the tokens,
+//    accumulated by one more product per tile against a constant 136 operand
+//    with the same bf16 probabilities, and subtracted at the end.  For K each
+//    lane group holds d/4 contiguous dims of its token; a k-step takes one
+//    dword (8 dims) in the order even dims, then odd dims, and the query
+//    operand is permuted the same way.  For V one transposed read yields both
+//    nibbles of a byte column: the low nibbles (even dims) and the high
+//    nibbles (odd dims) feed two products.
 #include "device_util.h"
 #include "launch.h"
 
@@ -69,7 +73,7 @@ struct SplitParams {
   int nhc;      // head chunks per kv head: ceil(G / 16)
   int nsplit;
   int chunk;    // tokens per split
-  float c;      // scale * log2(e) (divided by 16 for int4 codes)
+  float c;      // scale * log2(e)
 };
 
 // Byte counts of one tile for a code width.
@@ -85,21 +89,39 @@ struct Geom {
   static constexpr int NREAD = RB / 16;           // transposed V reads per tile
 };
 
-// KB bytes at src as dwords w[0 .. KB/4) (zero when !ok: past the split end).
+// bf16 of (136 + code) for 8 int4 codes: element e of lo4 / hi4 is the code
+// in the low nibble of byte e (already 0 .. 15 = code + 8).  The two results'
+// slot order is: bytes 0, 1 of the first source, bytes 2, 3, then the second.
+constexpr uint32_t kBf16Hi128 = 0x43434343u;  // high byte of bf16 128 .. 255
+__device__ __forceinline__ bf16x8 biased_bf16x8(uint32_t a4, uint32_t b4) {
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(kBf16Hi128, a4, 0x04010400u);  // [a.b0, 0x43, a.b1, 0x43]
+  r.y = __builtin_amdgcn_perm(kBf16Hi128, a4, 0x04030402u);  // [a.b2, 0x43, a.b3, 0x43]
+  r.z = __builtin_amdgcn_perm(kBf16Hi128, b4, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(kBf16Hi128, b4, 0x04030402u);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// KB bytes at src as dwords w[0 .. KB/4).
 template <int KB>
-__device__ __forceinline__ void load_k(const uint8_t* src, bool ok, uint32_t* w) {
+__device__ __forceinline__ void load_k(const uint8_t* src, uint32_t* w) {
   if constexpr (KB % 16 == 0) {
 #pragma unroll
     for (int i = 0; i < KB / 16; ++i) {
-      const uint4 x = ok ? reinterpret_cast<const uint4*>(src)[i] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 x = reinterpret_cast<const uint4*>(src)[i];
       w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
     }
   } else {
     static_assert(KB == 8, "a quarter row is 8, 16 or 32 bytes");
-    const uint2 x = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
+    const uint2 x = *reinterpret_cast<const uint2*>(src);
     w[0] = x.x; w[1] = x.y;
   }
 }
+
+// Register-ring depth: tiles in flight = slots - 1.  An int8 slot takes 33
+// VGPRs (a fifth slot spills), an int4 slot 17; measured on MI355X with one
+// wave per SIMD, 6 or 8 int4 slots were no faster than 4.
+constexpr int kRingSlots = 4;
 
 // Loads of one 32-token tile held in registers between issue and use.
 template <int D, int BITS>
@@ -169,8 +191,13 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
     }
   }
 
-  // Tile loads (plain global loads into registers; tokens past the split end
-  // read as zero).  Issued three tiles ahead of use.
+  // Tile loads (plain global loads into registers), issued three tiles ahead
+  // of use.  Every load is unconditional: a token past the split end reads
+  // the split's last token instead (its score is masked to -inf below, so its
+  // probability is exactly 0 and its finite codes and scales add nothing).  A
+  // load under a lane condition would become a branch, after which the
+  // compiler can no longer count outstanding loads and waits for all of them
+  // before every tile, which would empty the ring.
   const int v_row = lane / CPR, v_col = 16 * (lane % CPR);
   const float* sc_src = lane < kTile ? ksb : vsb;
   const int sc_tok = lane & (kTile - 1);
@@ -178,29 +205,41 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
     const int t0 = t_begin + t * kTile;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int tok = t0 + 16 * blk + n;
+      const int tok = min(t0 + 16 * blk + n, t_end - 1);
       const uint8_t* krow = kbase + int64_t(tok) * RB;
       if constexpr (BITS == 8) {
 #pragma unroll
-        for (int u = 0; u < KB / 16; ++u) load_k<16>(krow + 16 * (g + 4 * u), tok < t_end, &r.k[blk][4 * u]);
+        for (int u = 0; u < KB / 16; ++u) load_k<16>(krow + 16 * (g + 4 * u), &r.k[blk][4 * u]);
       } else {
-        load_k<KB>(krow + KB * g, tok < t_end, r.k[blk]);
+        load_k<KB>(krow + KB * g, r.k[blk]);
       }
     }
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int tok = t0 + i * RPL + v_row;
-      r.v[i] = tok < t_end ? *reinterpret_cast<const uint4*>(vbase + int64_t(tok) * RB + v_col)
-                           : make_uint4(0u, 0u, 0u, 0u);
+      const int tok = min(t0 + i * RPL + v_row, t_end - 1);
+      r.v[i] = *reinterpret_cast<const uint4*>(vbase + int64_t(tok) * RB + v_col);
     }
-    const int stok = t0 + sc_tok;
-    r.sc = stok < t_end ? sc_src[stok] : 0.f;
+    r.sc = sc_src[min(t0 + sc_tok, t_end - 1)];
   };
 
   f32x4 acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4{};
   float m_run = kNegHuge, l_run = 0.f;
+
+  // int4: the value operand carries +136 per element; pbias accumulates the
+  // matching 136 * sum(p') and kbias is the score bias 136 * sum(q) of this
+  // lane's head (every row of these products holds the same number).
+  const bf16x8 c136 = __builtin_bit_cast(bf16x8, make_uint4(0x43084308u, 0x43084308u,
+                                                            0x43084308u, 0x43084308u));
+  f32x4 pbias = f32x4{};
+  float kbias = 0.f;
+  if constexpr (BITS == 4) {
+    f32x4 kb = f32x4{};
+#pragma unroll
+    for (int m = 0; m < KM; ++m) kb = mfma16(c136, qf[m], kb);
+    kbias = kb[0];
+  }
 
   // P^T slot e of lane group g is token 4g + e (e < 4) or 16 + 4g + (e - 4);
   // source lane s of the group addresses that token's V row (tr8 read).
@@ -228,9 +267,9 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
         bf16x8 a;
         if constexpr (BITS == 8) {
           a = i8x8_to_bf16x8(r.k[blk][2 * m], r.k[blk][2 * m + 1]);
-        } else {  // 16 * code: even dims of the dword, then odd dims
-          const uint32_t w = r.k[blk][m];
-          a = i8x8_to_bf16x8((w << 4) & 0xf0f0f0f0u, w & 0xf0f0f0f0u);
+        } else {  // 136 + code: even dims of the dword, then odd dims
+          const uint32_t t4 = r.k[blk][m] ^ 0x88888888u;
+          a = biased_bf16x8(t4 & 0x0f0f0f0fu, (t4 >> 4) & 0x0f0f0f0fu);
         }
         s[blk] = mfma16(a, qf[m], s[blk]);
       }
@@ -242,8 +281,8 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
     float tv[8];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      tv[rr] = s[0][rr] * (ks0[rr] * p.c);
-      tv[4 + rr] = s[1][rr] * (ks1[rr] * p.c);
+      tv[rr] = (s[0][rr] - kbias) * (ks0[rr] * p.c);
+      tv[4 + rr] = (s[1][rr] - kbias) * (ks1[rr] * p.c);
     }
     if (t0 + kTile > t_end) {  // ragged last tile: tokens past the end are not keys
 #pragma unroll
@@ -264,6 +303,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
       l_run *= alpha;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
+      if constexpr (BITS == 4) pbias *= alpha;
     }
     const f32x4 vs0 = *reinterpret_cast<const f32x4*>(slds + kTile + 4 * g);
     const f32x4 vs1 = *reinterpret_cast<const f32x4*>(slds + kTile + 16 + 4 * g);
@@ -284,39 +324,41 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
       if constexpr (BITS == 8) {
         acc[cb] = mfma16(i8x8_to_bf16x8(r0w, r1w), pf, acc[cb]);
       } else {  // byte column 16cb + t: even dim from the low nibbles, odd from the high
-        acc[2 * cb] = mfma16(i8x8_to_bf16x8((r0w << 4) & 0xf0f0f0f0u, (r1w << 4) & 0xf0f0f0f0u),
-                             pf, acc[2 * cb]);
-        acc[2 * cb + 1] = mfma16(i8x8_to_bf16x8(r0w & 0xf0f0f0f0u, r1w & 0xf0f0f0f0u), pf,
-                                 acc[2 * cb + 1]);
+        const uint32_t t0 = r0w ^ 0x88888888u, t1 = r1w ^ 0x88888888u;
+        acc[2 * cb] = mfma16(biased_bf16x8(t0 & 0x0f0f0f0fu, t1 & 0x0f0f0f0fu), pf, acc[2 * cb]);
+        acc[2 * cb + 1] = mfma16(biased_bf16x8((t0 >> 4) & 0x0f0f0f0fu, (t1 >> 4) & 0x0f0f0f0fu),
+                                 pf, acc[2 * cb + 1]);
       }
     }
+    if constexpr (BITS == 4) pbias = mfma16(c136, pf, pbias);
   };
 
-  // four-slot register ring: tiles t+1 .. t+3 are in flight while t is processed
-  TileRegs<D, BITS> r0, r1, r2, r3;
-  if (0 < ntiles) load_tile(0, r0);
-  if (1 < ntiles) load_tile(1, r1);
-  if (2 < ntiles) load_tile(2, r2);
-  for (int t = 0; t < ntiles; t += 4) {
-    if (t + 3 < ntiles) load_tile(t + 3, r3);
-    process(t, r0);
-    if (t + 1 >= ntiles) break;
-    if (t + 4 < ntiles) load_tile(t + 4, r0);
-    process(t + 1, r1);
-    if (t + 2 >= ntiles) break;
-    if (t + 5 < ntiles) load_tile(t + 5, r1);
-    process(t + 2, r2);
-    if (t + 3 >= ntiles) break;
-    if (t + 6 < ntiles) load_tile(t + 6, r2);
-    process(t + 3, r3);
+  // four-slot register ring: tiles t+1 .. t+3 are in flight while t is
+  // processed.  Slots are refilled unconditionally (a tile past the end
+  // rereads the split's last token, cached): with a fixed load sequence the
+  // compiler waits only for the slot about to be used.
+  // (An empty split, which the split plan never makes, skips the ring and
+  // writes o = 0, lse = -inf below.)
+  if (ntiles > 0) {
+    constexpr int NS = kRingSlots;
+    TileRegs<D, BITS> ring[NS];
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) load_tile(j, ring[j]);
+    for (int t = 0; t < ntiles; t += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {  // slot indices are compile-time after unrolling
+        if (j > 0 && t + j >= ntiles) break;
+        load_tile(t + j + NS - 1, ring[(j + NS - 1) % NS]);
+        process(t + j, ring[j]);
+      }
+    }
   }
 
   // row sum over the four lane groups holding this head's tokens
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (!head_ok) return;
-  // int4 values entered as 16 * code: the factor leaves with the normalisation
-  const float inv = l_tot > 0.f ? (BITS == 8 ? 1.f : 0.0625f) / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t prow = (int64_t(b) * p.Hq + hq) * p.nsplit + split;
   float* po = p.part_o + prow * D;
   if constexpr (BITS == 8) {
@@ -328,8 +370,9 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   } else {
 #pragma unroll
     for (int cb = 0; cb < GM::NREAD; ++cb) {
-      // acc[2cb][r] / acc[2cb+1][r]: dims 32*cb + 8g + 2r and that + 1
-      const f32x4 e = acc[2 * cb] * inv, o = acc[2 * cb + 1] * inv;
+      // acc[2cb][r] / acc[2cb+1][r]: dims 32*cb + 8g + 2r and that + 1, each
+      // carrying the bias 136 * sum(p') that pbias holds in every register
+      const f32x4 e = (acc[2 * cb] - pbias) * inv, o = (acc[2 * cb + 1] - pbias) * inv;
       *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
       *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
     }
@@ -396,7 +439,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.nhc = (p.G + kHeadsPerWave - 1) / kHeadsPerWave;
   p.nsplit = a.nsplit;
   p.chunk = a.chunk;
-  p.c = a.scale * 1.4426950408889634f * (a.bits == 8 ? 1.f : 0.0625f);
+  p.c = a.scale * 1.4426950408889634f;
   const int64_t waves = int64_t(a.B) * a.Hkv * p.nhc * a.nsplit;
   const int64_t rows = int64_t(a.B) * a.Hq;
   if (waves > 0x7fffffff || rows > 0x7fffffff) return hipErrorInvalidConfiguration;

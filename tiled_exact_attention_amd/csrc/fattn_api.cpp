@@ -33,14 +33,16 @@ bool supported_head_dim(int d) { return d == 64 || d == 128; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Automatic split count.  The split kernel runs one wave per (b, kv head,
-// chunk of <= 16 query heads, split) at two waves per SIMD, so MI355X holds
-// 256 CUs x 4 SIMDs x 2 = 2048 of them at once.  Measured on MI355X, the
-// fastest plan fills exactly one round of resident waves: a partial second
-// round leaves most of the chip idle while it drains (9 or 10 splits of the
-// B=32, Hkv=8, 32K-token cache run 25-30% slower than 8).  So the count is the
-// largest that keeps all waves resident, with each split >= 256 tokens.  A pure
-// function of the arguments (no device query), so the workspace size is known
-// on the host before any device work.
+// chunk of <= 16 query heads, split) at up to two waves per SIMD, so MI355X
+// holds 256 CUs x 4 SIMDs x 2 = 2048 of them at once.  Measured on MI355X with
+// the B=32, Hkv=8, 32K-token cache: a partial second round of waves leaves
+// most of the chip idle while it drains (9 or 10 splits run 25-30% slower
+// than 8); one wave per SIMD (4 splits) is 2-5% faster on an idle chip but
+// 12% slower right after a prefill kernel, where two waves per SIMD hide the
+// slower start.  So the count is the largest that keeps all waves in one
+// round of 2048, with each split >= 256 tokens.  A pure function of the
+// arguments (no device query), so the workspace size is known on the host
+// before any device work.
 int auto_splits(int B, int Hq, int Hkv, int Skv) {
   const int64_t resident_waves = 2048;
   const int64_t head_chunks = (int64_t(Hq / Hkv) + 15) / 16;
