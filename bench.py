@@ -12,6 +12,10 @@ algorithmic bytes (int8 K and V, their fp32 scales, the bf16 query and output).
 Each kernel call is timed with HIP events recorded on the stream it runs on
 (torch's current stream, which the binding passes to libfattn).
 
+After the timed steps, the next rows of the path are timed the same way
+(informational, under "next"): decode over an int4 cache of the decode
+workload's shape, and the int8 / int4 cache append of one 32K-token tensor.
+
 The CPU baseline times the fp64 oracle on the host on a bounded sample of the
 prefill workload (whole query rows of a few (batch, head) pairs).
 
@@ -61,7 +65,7 @@ def prefill_flops(w):
 
 
 def decode_bytes(w):
-    kv = 2 * w.B * w.Hkv * w.Skv * w.d          # int8 codes of K and V
+    kv = 2 * w.B * w.Hkv * w.Skv * w.d * w.bits // 8   # codes of K and V (int8 or packed int4)
     scales = 2 * w.B * w.Hkv * w.Skv * 4         # fp32 scales
     qo = 2 * w.B * w.Hq * w.d * 2                # bf16 query and output
     return kv + scales + qo
@@ -304,31 +308,54 @@ def main():
     if args.only == "all":
         # next rows of the path, each timed the same way (informational)
         result["next"] = {}
-        # int8 KV-cache append: quantise one tensor (K) of the decode workload's 32K-token cache
         del dq, dkq, dks, dvq, dvs
         torch.cuda.empty_cache()
+
+        def time_calls(fn, reps=10):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        def hbm_entry(workload, us, nbytes):
+            return {"workload": workload, "us": round(us, 2),
+                    "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                    "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "algorithmic_bytes": nbytes}
+
+        # decode over the int4 cache of the same shape (two codes per byte)
+        w4 = W.INT4_DECODE
+        log(f"generating {w4.name}")
+        q4, k4, ks4, v4, vs4 = W.decode_workload_inputs(w4, device=dev)
+        o4 = torch.empty_like(q4)
+        ws4 = torch.empty((fa.decode_workspace_size(w4.B, w4.Hq, w4.Hkv, w4.Skv, w4.d, 0),),
+                          dtype=torch.uint8, device=dev)
+        us = time_calls(lambda: fa.decode_int4(q4, k4, ks4, v4, vs4, scale=w4.scale, workspace=ws4,
+                                               out=o4), reps=20)
+        result["next"]["decode_int4"] = hbm_entry(w4.name, us, decode_bytes(w4))
+        del q4, k4, ks4, v4, vs4, o4, ws4
+        torch.cuda.empty_cache()
+
+        # KV-cache append: quantise one tensor (K) of the decode workload's 32K-token cache
         g = torch.Generator(device=dev)
         g.manual_seed(wd.seed)
         xk = torch.randn(wd.B, wd.Skv, wd.Hkv, wd.d, generator=g, device=dev).to(torch.bfloat16)
-        codes = torch.empty(wd.B, wd.Hkv, wd.Skv, wd.d, dtype=torch.int8, device=dev)
         scs = torch.empty(wd.B, wd.Hkv, wd.Skv, dtype=torch.float32, device=dev)
-        for _ in range(3):
-            fa.kv_append_int8(xk, codes, scs, pos=0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        e0.record(stream)
-        for _ in range(reps):
-            fa.kv_append_int8(xk, codes, scs, pos=0)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        nbytes = xk.numel() * 2 + codes.numel() + scs.numel() * 4
-        result["next"]["kv_append_int8"] = {
-            "workload": f"append B{wd.B} T{wd.Skv} Hkv{wd.Hkv} d{wd.d} bf16 -> int8 cache",
-            "us": round(us, 2), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "frac_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "algorithmic_bytes": nbytes}
-        del xk, codes, scs
+        for bits in (8, 4):
+            codes = torch.empty(wd.B, wd.Hkv, wd.Skv, wd.d * bits // 8,
+                                dtype=torch.int8 if bits == 8 else torch.uint8, device=dev)
+            append = fa.kv_append_int8 if bits == 8 else fa.kv_append_int4
+            us = time_calls(lambda: append(xk, codes, scs, pos=0))
+            nbytes = xk.numel() * 2 + codes.numel() + scs.numel() * 4
+            result["next"][f"kv_append_int{bits}"] = hbm_entry(
+                f"append B{wd.B} T{wd.Skv} Hkv{wd.Hkv} d{wd.d} bf16 -> int{bits} cache", us, nbytes)
+            del codes
+        del xk, scs
 
     if do_prefill and not args.no_cpu_baseline:
         log(f"cpu baseline: fp64 oracle, about {args.cpu_budget:.0f} s")
