@@ -52,7 +52,7 @@ def _load(path: str | None = None):
         lib.oracle_fwd_rows.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                         f64, i32, i32, vp, i64, vp, vp, i32]
         lib.oracle_fwd_rows.restype = i32
-        lib.oracle_decode_int8_rows.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+        lib.oracle_decode_int8_rows.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                 f64, vp, i64, vp, vp, i32]
         lib.oracle_decode_int8_rows.restype = i32
         lib.oracle_decode_int4_rows.argtypes = lib.oracle_decode_int8_rows.argtypes
@@ -61,6 +61,9 @@ def _load(path: str | None = None):
         lib.oracle_kv_quantize_int8.restype = i32
         lib.oracle_kv_quantize_int4.argtypes = lib.oracle_kv_quantize_int8.argtypes
         lib.oracle_kv_quantize_int4.restype = i32
+        lib.oracle_fwd_varlen_rows.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                               f64, i32, i32, vp, i64, vp, vp, i32]
+        lib.oracle_fwd_varlen_rows.restype = i32
         lib.oracle_max_threads.argtypes = [i32]
         lib.oracle_max_threads.restype = i32
         _libs[path] = lib
@@ -129,7 +132,49 @@ def fwd(q, k, v, *, causal: bool, window: int = 0, scale: float | None = None,
     return o, lse
 
 
-def _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, bits):
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool, window: int = 0,
+               scale: float | None = None, rows=None, threads: int = 0, lib: str | None = None):
+    """Exact attention over packed sequences of different lengths, in fp64.
+
+    q: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; cu_seqlens_q / cu_seqlens_k:
+    [B+1] cumulative lengths from 0.  Sequence b attends only within itself.
+    rows: None for every output row, else an int array [n, 2] of (h, i) pairs
+    with i a packed query row.  Returns (o, lse): o [total_q, Hq, d] and lse
+    [Hq, total_q], or [n, d] and [n] for explicit rows.
+    """
+    qd, kd, vd = _f64(q), _f64(k), _f64(v)
+    total_q, Hq, d = qd.shape
+    total_k, Hkv, dk = kd.shape
+    if dk != d or vd.shape != kd.shape:
+        raise ValueError("shape mismatch between q, k and v")
+    cq = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int32))
+    ck = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int32))
+    if cq.shape != ck.shape or cq.ndim != 1 or cq.size < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    B = cq.size - 1
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    full = rows is None
+    if full:
+        hh, ii = np.meshgrid(np.arange(Hq), np.arange(total_q), indexing="ij")
+        rows = np.stack([hh.ravel(), ii.ravel()], axis=1)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    n = rows.shape[0]
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty((n,), dtype=np.float64)
+    rc = _load(lib).oracle_fwd_varlen_rows(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(cq), _ptr(ck), B, Hq,
+                                           Hkv, total_q, total_k, d, float(scale),
+                                           int(bool(causal)), int(window), _ptr(rows), n,
+                                           _ptr(o), _ptr(lse), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_fwd_varlen_rows rejected its arguments (code {rc})")
+    if full:
+        o = o.reshape(Hq, total_q, d).transpose(1, 0, 2).copy()
+        lse = lse.reshape(Hq, total_q)
+    return o, lse
+
+
+def _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, bits, seqlens=None):
     qd = _f64(q)
     code_t = np.int8 if bits == 8 else np.uint8
     kqa, vqa = _np(kq, code_t), _np(vq, code_t)
@@ -150,9 +195,14 @@ def _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, bits):
     n = rows.shape[0]
     o = np.empty((n, d), dtype=np.float64)
     lse = np.empty((n,), dtype=np.float64)
+    sl = None
+    if seqlens is not None:
+        sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+        if sl.shape != (B,):
+            raise ValueError("seqlens must be [B]")
     fn = _load(lib).oracle_decode_int8_rows if bits == 8 else _load(lib).oracle_decode_int4_rows
-    rc = fn(_ptr(qd), _ptr(kqa), _ptr(ksa), _ptr(vqa), _ptr(vsa), B, Hq, Hkv, Skv, d, float(scale),
-            _ptr(rows), n, _ptr(o), _ptr(lse), int(threads))
+    rc = fn(_ptr(qd), _ptr(kqa), _ptr(ksa), _ptr(vqa), _ptr(vsa), None if sl is None else _ptr(sl),
+            B, Hq, Hkv, Skv, d, float(scale), _ptr(rows), n, _ptr(o), _ptr(lse), int(threads))
     if rc != 0:
         raise ValueError(f"oracle decode (int{bits}) rejected its arguments (code {rc})")
     if full:
@@ -161,27 +211,28 @@ def _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, bits):
     return o, lse
 
 
-def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
+def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, seqlens=None,
                 rows=None, threads: int = 0, lib: str | None = None):
     """Decode attention of one query token over an int8 KV cache, in fp64.
 
     q: [B, Hq, d] (widened to fp64); kq, vq: [B, Hkv, Skv, d] int8;
-    k_scale, v_scale: [B, Hkv, Skv] float32.  Every cached key is visible.
+    k_scale, v_scale: [B, Hkv, Skv] float32.  Every cached key is visible,
+    or with seqlens ([B] ints) the first seqlens[b] keys of sequence b.
     rows: None for all (b, h), else an int array [n, 2] of (b, h) pairs.
     Returns (o, lse) shaped [B, Hq, d] and [B, Hq], or [n, d] and [n].
     lib: path of an alternative build of the oracle source (tests only).
     """
-    return _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, 8)
+    return _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, 8, seqlens)
 
 
-def decode_int4(q, kq, k_scale, vq, v_scale, *, scale: float | None = None,
+def decode_int4(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, seqlens=None,
                 rows=None, threads: int = 0, lib: str | None = None):
     """Decode attention over an int4 KV cache, in fp64 (as decode_int8).
 
     kq, vq: [B, Hkv, Skv, d/2] uint8, two signed 4-bit codes per byte
     (element 2i in the low nibble of byte i, element 2i+1 in the high one).
     """
-    return _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, 4)
+    return _decode(q, kq, k_scale, vq, v_scale, scale, rows, threads, lib, 4, seqlens)
 
 
 def _kv_quantize(x, codes, scales, pos, cap, lib, bits):

@@ -204,6 +204,74 @@ int oracle_fwd_rows(const double* q, const double* k, const double* v,
 }
 
 /*
+ * Prefill over packed sequences of different lengths ([FA-3MOVES] names
+ * variable-length batches as a CANN feature without a layout; the packed
+ * layout with cumulative offsets is a reading).  Sequence b owns query rows
+ * cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1 and attends only
+ * within itself, with the causal / window rules above applied to its own
+ * lengths (Sq_b = cu_q[b+1] - cu_q[b], Skv_b likewise).  Layouts:
+ *   q [total_q, Hq, d], k and v [total_k, Hkv, d];  cu_q, cu_k [B+1],
+ *   non-decreasing from 0 to total_q / total_k.
+ * rows: nrows pairs (h, i) with i a packed query row.  o: nrows x d, lse: nrows.
+ */
+int oracle_fwd_varlen_rows(const double* q, const double* k, const double* v,
+                           const int* cu_q, const int* cu_k,
+                           int B, int Hq, int Hkv, int total_q, int total_k, int d,
+                           double scale, int causal, int window,
+                           const int64_t* rows, int64_t nrows,
+                           double* o, double* lse, int nthreads) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 0 || total_k < 0 || d < 1 || Hq % Hkv != 0) return ORACLE_BAD_ARGS;
+  if (window < 0 || (window > 0 && !causal)) return ORACLE_BAD_ARGS;
+  if (!q || !k || !v || !cu_q || !cu_k || !rows || !o || !lse || nrows < 0) return ORACLE_BAD_ARGS;
+  if (cu_q[0] != 0 || cu_k[0] != 0 || cu_q[B] != total_q || cu_k[B] != total_k) return ORACLE_BAD_ARGS;
+  for (int b = 0; b < B; b++) {
+    if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return ORACLE_BAD_ARGS;
+  }
+  for (int64_t r = 0; r < nrows; r++) {
+    int64_t h = rows[2 * r], i = rows[2 * r + 1];
+    if (h < 0 || h >= Hq || i < 0 || i >= total_q) return ORACLE_BAD_ARGS;
+  }
+  int group = Hq / Hkv;
+  int64_t max_skv = 1;
+  for (int b = 0; b < B; b++) {
+    if (cu_k[b + 1] - cu_k[b] > max_skv) max_skv = cu_k[b + 1] - cu_k[b];
+  }
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)max_skv);
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; r++) {
+      if (!s) continue;
+      int64_t h = rows[2 * r], i = rows[2 * r + 1];
+      int b = 0; /* the sequence holding packed row i */
+      while (cu_q[b + 1] <= i) b++;
+      int sq = cu_q[b + 1] - cu_q[b], skv = cu_k[b + 1] - cu_k[b];
+      int64_t hk = h / group;
+      int64_t jlo, jhi;
+      visible_range(i - cu_q[b], sq, skv, causal, window, &jlo, &jhi);
+      const double* qrow = q + (i * Hq + h) * (int64_t)d;
+      int64_t kv_stride = (int64_t)Hkv * d;
+      const double* kb = k + ((int64_t)cu_k[b] * Hkv + hk) * (int64_t)d;
+      const double* vb = v + ((int64_t)cu_k[b] * Hkv + hk) * (int64_t)d;
+      attend_row(qrow, d, scale, jlo, jhi, kb, vb, kv_stride, NULL, NULL, NULL, NULL, 0,
+                 s, o + r * (int64_t)d, lse + r);
+    }
+    free(s);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
  * Decode over a quantised KV cache: one new query token per sequence, every
  * cached key visible.  Layouts:
  *   q [B, Hq, d];  kq, vq [B, Hkv, Skv, row_bytes] codes (row_bytes = d for
@@ -211,7 +279,7 @@ int oracle_fwd_rows(const double* q, const double* k, const double* v,
  * rows: nrows pairs (b, h).  o: nrows x d, lse: nrows.
  */
 static int decode_rows(const double* q, const uint8_t* kq, const float* ks,
-                       const uint8_t* vq, const float* vs,
+                       const uint8_t* vq, const float* vs, const int* seqlens,
                        int B, int Hq, int Hkv, int Skv, int d, double scale,
                        const int64_t* rows, int64_t nrows,
                        double* o, double* lse, int nthreads, int bits) {
@@ -221,6 +289,11 @@ static int decode_rows(const double* q, const uint8_t* kq, const float* ks,
   for (int64_t r = 0; r < nrows; r++) {
     int64_t b = rows[2 * r], h = rows[2 * r + 1];
     if (b < 0 || b >= B || h < 0 || h >= Hq) return ORACLE_BAD_ARGS;
+  }
+  if (seqlens) {
+    for (int b = 0; b < B; b++) {
+      if (seqlens[b] < 0 || seqlens[b] > Skv) return ORACLE_BAD_ARGS;
+    }
   }
   int group = Hq / Hkv;
   int64_t row_bytes = bits == 8 ? d : d / 2;
@@ -244,7 +317,8 @@ static int decode_rows(const double* q, const uint8_t* kq, const float* ks,
       int64_t hk = h / group;
       int64_t stream = b * Hkv + hk;
       const double* qrow = q + (b * Hq + h) * (int64_t)d;
-      attend_row(qrow, d, scale, 0, Skv, NULL, NULL, 0,
+      int64_t len = seqlens ? seqlens[b] : Skv; /* sequence b sees its first len cached tokens */
+      attend_row(qrow, d, scale, 0, len, NULL, NULL, 0,
                  kq + stream * Skv * row_bytes, vq + stream * Skv * row_bytes,
                  ks + stream * Skv, vs + stream * Skv, bits,
                  s, o + r * (int64_t)d, lse + r);
@@ -254,23 +328,26 @@ static int decode_rows(const double* q, const uint8_t* kq, const float* ks,
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 
-/* int8 cache: kq, vq [B, Hkv, Skv, d] int8. */
+/* int8 cache: kq, vq [B, Hkv, Skv, d] int8.  seqlens: NULL (every sequence
+ * sees all Skv cached tokens) or [B] lengths, 0 <= seqlens[b] <= Skv (a
+ * variable-length batch, [FA-3MOVES] CANN feature list). */
 int oracle_decode_int8_rows(const double* q, const int8_t* kq, const float* ks,
-                            const int8_t* vq, const float* vs,
+                            const int8_t* vq, const float* vs, const int* seqlens,
                             int B, int Hq, int Hkv, int Skv, int d, double scale,
                             const int64_t* rows, int64_t nrows,
                             double* o, double* lse, int nthreads) {
-  return decode_rows(q, (const uint8_t*)kq, ks, (const uint8_t*)vq, vs, B, Hq, Hkv, Skv, d, scale,
-                     rows, nrows, o, lse, nthreads, 8);
+  return decode_rows(q, (const uint8_t*)kq, ks, (const uint8_t*)vq, vs, seqlens, B, Hq, Hkv, Skv,
+                     d, scale, rows, nrows, o, lse, nthreads, 8);
 }
 
 /* int4 cache: kq, vq [B, Hkv, Skv, d/2] bytes, two codes each; d even. */
 int oracle_decode_int4_rows(const double* q, const uint8_t* kq, const float* ks,
-                            const uint8_t* vq, const float* vs,
+                            const uint8_t* vq, const float* vs, const int* seqlens,
                             int B, int Hq, int Hkv, int Skv, int d, double scale,
                             const int64_t* rows, int64_t nrows,
                             double* o, double* lse, int nthreads) {
-  return decode_rows(q, kq, ks, vq, vs, B, Hq, Hkv, Skv, d, scale, rows, nrows, o, lse, nthreads, 4);
+  return decode_rows(q, kq, ks, vq, vs, seqlens, B, Hq, Hkv, Skv, d, scale, rows, nrows, o, lse,
+                     nthreads, 4);
 }
 
 /*

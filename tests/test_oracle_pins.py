@@ -503,6 +503,95 @@ def pin_int4_quantizer_matches_torch(lib):
     assert np.array_equal(sc.transpose(0, 2, 1), s_ref.numpy())
 
 
+def brute_force_varlen(q, k, v, cu_q, cu_k, causal, window, scale):
+    """Full packed [total_q, total_k] score matrix with a block-diagonal mask:
+    query row i and key row j interact only inside the same sequence."""
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[:2]
+    G = Hq // Hkv
+    cu_q, cu_k = np.asarray(cu_q), np.asarray(cu_k)
+    sq_of = np.searchsorted(cu_q, np.arange(total_q), side="right") - 1
+    sk_of = np.searchsorted(cu_k, np.arange(total_k), side="right") - 1
+    pq = np.arange(total_q) - cu_q[sq_of]
+    pk = np.arange(total_k) - cu_k[sk_of]
+    off = (cu_k[sq_of + 1] - cu_k[sq_of]) - (cu_q[sq_of + 1] - cu_q[sq_of])
+    vis = sq_of[:, None] == sk_of[None, :]
+    if causal:
+        vis &= pk[None, :] <= pq[:, None] + off[:, None]
+        if window:
+            vis &= pk[None, :] > pq[:, None] + off[:, None] - window
+    o = np.zeros((total_q, Hq, d))
+    lse = np.full((Hq, total_q), -np.inf)
+    for h in range(Hq):
+        s = np.where(vis, scale * (q[:, h] @ k[:, h // G].T), -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        ok = np.isfinite(m[:, 0])
+        e = np.where(vis, np.exp(s - np.where(np.isfinite(m), m, 0.0)), 0.0)
+        l = e.sum(axis=1, keepdims=True)
+        o[:, h] = np.divide(e, l, out=np.zeros_like(e), where=l > 0) @ v[:, h // G]
+        lse[h, ok] = (m[:, 0] + np.log(l[:, 0]))[ok]
+    return o, lse
+
+
+def pin_varlen_block_diagonal_brute_force(lib):
+    # lengths with an empty query sequence, Sq < Skv and Sq > Skv (bottom-right
+    # alignment per sequence), a key-less sequence, GQA
+    lq = [5, 0, 3, 9, 4, 2]
+    lk = [5, 2, 7, 6, 0, 2]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    Hq, Hkv, d = 4, 2, 8
+    q = _rand((cu_q[-1], Hq, d), 57)
+    k, v = _rand((cu_k[-1], Hkv, d), 58), _rand((cu_k[-1], Hkv, d), 59)
+    for causal, window in ((False, 0), (True, 0), (True, 3)):
+        o, lse = oracle.fwd_varlen(q, k, v, cu_q, cu_k, causal=causal, window=window, scale=0.35, lib=lib)
+        ob, lb = brute_force_varlen(q, k, v, cu_q, cu_k, causal, window, 0.35)
+        assert np.allclose(o, ob, atol=1e-12, rtol=0)
+        assert np.array_equal(np.isfinite(lse), np.isfinite(lb))
+        assert np.allclose(lse[np.isfinite(lb)], lb[np.isfinite(lb)], atol=1e-12, rtol=0)
+    # the key-less sequence (index 4): o = 0, lse = -inf
+    rows4 = slice(cu_q[4], cu_q[5])
+    assert np.all(o[rows4] == 0) and np.all(np.isneginf(lse[:, rows4]))
+
+
+def pin_varlen_equal_lengths_is_the_batch(lib):
+    B, S, Hq, Hkv, d = 3, 6, 4, 1, 8
+    q, k, v = _rand((B, S, Hq, d), 60), _rand((B, S, Hkv, d), 61), _rand((B, S, Hkv, d), 62)
+    cu = np.arange(B + 1) * S
+    for causal in (False, True):
+        o, lse = oracle.fwd_varlen(q.reshape(B * S, Hq, d), k.reshape(B * S, Hkv, d),
+                                   v.reshape(B * S, Hkv, d), cu, cu, causal=causal, lib=lib)
+        ob, lb = oracle.fwd(q, k, v, causal=causal, lib=lib)
+        assert np.array_equal(o, ob.reshape(B * S, Hq, d))
+        assert np.array_equal(lse, lb.transpose(1, 0, 2).reshape(Hq, B * S))
+
+
+def pin_decode_seqlens_attend_to_the_prefix(lib):
+    B, Hq, Hkv, Skv, d = 3, 4, 2, 13, 8
+    q = _rand((B, Hq, d), 63)
+    kq, ks = _quantise(_rand((B, Hkv, Skv, d), 64))
+    vq, vs = _quantise(_rand((B, Hkv, Skv, d), 65))
+    lens = np.array([13, 0, 5], dtype=np.int32)
+    o, lse = oracle.decode_int8(q, kq, ks, vq, vs, scale=0.3, seqlens=lens, lib=lib)
+    kd = kq.astype(np.float64) * ks.astype(np.float64)[..., None]
+    vd = vq.astype(np.float64) * vs.astype(np.float64)[..., None]
+    for b in range(B):
+        L = lens[b]
+        if L == 0:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+            continue
+        ob, lb = brute_force(q[b:b + 1, None], kd[b:b + 1, :, :L].transpose(0, 2, 1, 3),
+                             vd[b:b + 1, :, :L].transpose(0, 2, 1, 3), False, 0, 0.3)
+        assert np.allclose(o[b], ob[0, 0], atol=1e-12, rtol=0)
+        assert np.allclose(lse[b], lb[0, :, 0], atol=1e-12, rtol=0)
+    # int4: same prefix rule
+    k4 = np.random.default_rng(66).integers(0, 256, (B, Hkv, Skv, d // 2), dtype=np.uint8)
+    o4, l4 = oracle.decode_int4(q, k4, ks, k4, vs, scale=0.3, seqlens=lens, lib=lib)
+    o4f, l4f = oracle.decode_int4(q[2:3], k4[2:3, :, :5].copy(), ks[2:3, :, :5].copy(),
+                                  k4[2:3, :, :5].copy(), vs[2:3, :, :5].copy(), scale=0.3, lib=lib)
+    assert np.array_equal(o4[2], o4f[0]) and np.array_equal(l4[2], l4f[0])
+    assert np.all(o4[1] == 0) and np.all(np.isneginf(l4[1]))
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -516,7 +605,9 @@ def test_pin(pin):
 # ----------------------------------------------------------------------------
 
 MUTANTS = {
-    "gqa head h % Hkv": ("int64_t hk = h / group;\n      int64_t jlo", "int64_t hk = h % Hkv;\n      int64_t jlo"),
+    "gqa head h % Hkv": ("i = rows[3 * r + 2];\n      int64_t hk = h / group;",
+                         "i = rows[3 * r + 2];\n      int64_t hk = h % Hkv;"),
+    "varlen gqa head h % Hkv": ("cu_k[b];\n      int64_t hk = h / group;", "cu_k[b];\n      int64_t hk = h % Hkv;"),
     "scale dropped": ("s[j - jlo] = scale * acc;", "s[j - jlo] = acc;"),
     "causal excludes the diagonal": ("hi = last + 1;", "hi = last;"),
     "window keeps W+1 keys": ("lo = last - window + 1;", "lo = last - window;"),
@@ -540,6 +631,12 @@ MUTANTS = {
     "int4 rows strided like int8": ("const int64_t row_bytes = bits == 8 ? d : d / 2;",
                                     "const int64_t row_bytes = d;"),
     "int4 packing high nibble first": ("(c % 2 == 0 ? nib : nib << 4)", "(c % 2 == 0 ? nib << 4 : nib)"),
+    "varlen positions not relative to the sequence": ("visible_range(i - cu_q[b], sq, skv,",
+                                                      "visible_range(i, sq, skv,"),
+    "varlen row lookup off by one": ("while (cu_q[b + 1] <= i) b++;", "while (cu_q[b + 1] < i) b++;"),
+    "varlen keys of the first sequence": ("const double* kb = k + ((int64_t)cu_k[b] * Hkv + hk) * (int64_t)d;",
+                                          "const double* kb = k + ((int64_t)cu_k[0] * Hkv + hk) * (int64_t)d;"),
+    "decode ignores seqlens": ("int64_t len = seqlens ? seqlens[b] : Skv;", "int64_t len = Skv;"),
     "quantiser rounds half away from zero": ("float r = rintf(qv);", "float r = roundf(qv);"),
     "quantiser ignores the append position": ("int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;",
                                              "int64_t slot = (b * Hkv + h) * (int64_t)cap + t;"),
