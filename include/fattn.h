@@ -95,6 +95,30 @@ FATTN_API int fattn_fwd(const void* q, const void* k, const void* v, void* o, fl
               float scale, int causal, int window, int dtype, void* stream);
 
 /*
+ * Exact attention over a packed batch of sequences of different lengths (the
+ * variable-length batches [FA-3MOVES] lists among CANN's features; the packed
+ * layout with cumulative offsets is the library's).  Sequence b owns query
+ * rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key/value rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 and attends only within itself;
+ * causal and window are those of fattn_fwd applied to each sequence's own
+ * lengths (Sq_b, Skv_b), so the causal diagonal ends at its last key.  A
+ * sequence with no keys gets o = 0 and lse = -inf.
+ *
+ * q, o   [total_q, Hq, d];  k, v [total_k, Hkv, d]   (dtype as in fattn_fwd)
+ * lse    [Hq, total_q] fp32 (natural log) or NULL
+ * cu_seqlens_q, cu_seqlens_k  [B+1] int32 device arrays, non-decreasing from
+ *        0 to total_q / total_k.  They live on the device and are not checked
+ *        on the host: offsets out of range are clamped into the tensors (the
+ *        kernels never address outside them) but give unspecified results.
+ * max_seqlen_q  >= every Sq_b (rows past it are not computed); <= total_q.
+ * total_q = 0 is a valid empty call.  Other rules and errors as fattn_fwd.
+ */
+FATTN_API int fattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int* cu_seqlens_q, const int* cu_seqlens_k,
+                     int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                     int d, float scale, int causal, int window, int dtype, void* stream);
+
+/*
  * Decode over an int8 KV cache ([FA-3MOVES] move 3: the cache stays
  * compressed and is used as is).  One new query token per sequence attends
  * to all Skv cached tokens.  The cache holds per (token, kv head) an int8 row
@@ -142,6 +166,27 @@ FATTN_API int fattn_decode_int4(const void* q, const uint8_t* kq, const float* k
                       int B, int Hq, int Hkv, int Skv, int d, float scale,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/*
+ * Decode over a cache whose sequences hold different numbers of tokens (a
+ * variable-length batch, [FA-3MOVES] CANN feature list): as
+ * fattn_decode_int8 / fattn_decode_int4, with sequence b attending to its
+ * first seqlens[b] cached tokens only.  Skv is the cache capacity (the
+ * tensors' token dimension); the split plan and workspace size are those of
+ * the capacity (fattn_decode_num_splits / _workspace_size with Skv).
+ *
+ * seqlens  [B] int32 device array, 0 <= seqlens[b] <= Skv; not checked on the
+ *          host (values outside are clamped into [0, Skv]).  A sequence with
+ *          0 tokens gets o = 0 and lse = -inf.
+ */
+FATTN_API int fattn_decode_int8_varlen(const void* q, const int8_t* kq, const float* k_scale,
+                      const int8_t* vq, const float* v_scale, const int* seqlens, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+FATTN_API int fattn_decode_int4_varlen(const void* q, const uint8_t* kq, const float* k_scale,
+                      const uint8_t* vq, const float* v_scale, const int* seqlens, void* o,
+                      float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Appends T new tokens to an int8 KV cache (the step that fills the cache

@@ -46,7 +46,8 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == sorted(["fattn_fwd", "fattn_decode_int8", "fattn_decode_int4",
+    assert names == sorted(["fattn_fwd", "fattn_fwd_varlen", "fattn_decode_int8", "fattn_decode_int4",
+                            "fattn_decode_int8_varlen", "fattn_decode_int4_varlen",
                             "fattn_decode_num_splits", "fattn_decode_workspace_size",
                             "fattn_kv_append_int8", "fattn_kv_append_int4",
                             "fattn_status_string", "fattn_version"])
@@ -206,3 +207,46 @@ def test_int4_wrappers_check_the_packed_shape():
     s = torch.zeros(1, 2, 10)
     with pytest.raises(ValueError):
         fa.decode_int4(q, kq, s, kq, s)  # CPU tensors are rejected before any shape use
+
+
+def _fwdv(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cq=P, ck=P, B=2, Hq=4, Hkv=2, tq=10, tk=12, mq=6, d=64,
+             scale=0.1, causal=1, window=0, dtype=1, stream=None)
+    a.update(kw)
+    return fa.fattn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"],
+                               a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"], a["d"], a["scale"],
+                               a["causal"], a["window"], a["dtype"], a["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,want", [
+    (dict(cq=None), FATTN_EINVAL), (dict(ck=None), FATTN_EINVAL), (dict(q=None), FATTN_EINVAL),
+    (dict(cq=P + 2), FATTN_EINVAL), (dict(lse=P + 2), FATTN_EINVAL), (dict(o=P + 4), FATTN_EINVAL),
+    (dict(B=0), FATTN_EINVAL), (dict(Hq=3), FATTN_EINVAL), (dict(tq=-1), FATTN_EINVAL),
+    (dict(tk=-1), FATTN_EINVAL), (dict(mq=11), FATTN_EINVAL), (dict(mq=0), FATTN_EINVAL),
+    (dict(mq=-1), FATTN_EINVAL), (dict(scale=math.nan), FATTN_EINVAL), (dict(causal=3), FATTN_EINVAL),
+    (dict(window=5, causal=0), FATTN_EINVAL), (dict(d=32), FATTN_EUNSUPPORTED),
+    (dict(dtype=2), FATTN_EUNSUPPORTED),
+    (dict(tq=0, mq=0), FATTN_OK),  # an empty batch is valid and launches nothing
+    (dict(tq=0, mq=0, q=None, o=None), FATTN_OK),  # ... also with null (empty) tensors
+    (dict(k=None), FATTN_EINVAL), (dict(v=None), FATTN_EINVAL),  # keys present, no k / v
+])
+def test_fwd_varlen_rejects_before_any_device_work(kw, want):
+    assert _fwdv(**kw) == want
+
+
+@no_gpu_only
+@pytest.mark.parametrize("fn", ["fattn_decode_int8_varlen", "fattn_decode_int4_varlen"])
+@pytest.mark.parametrize("kw,want", [
+    (dict(seqlens=None), FATTN_EINVAL), (dict(seqlens=P + 2), FATTN_EINVAL),
+    (dict(q=None), FATTN_EINVAL), (dict(Hq=3), FATTN_EINVAL), (dict(d=96), FATTN_EUNSUPPORTED),
+    (dict(ws=None), FATTN_EWORKSPACE),
+])
+def test_decode_varlen_rejects_before_any_device_work(fn, kw, want):
+    a = dict(q=P, kq=P, ks=P, vq=P, vs=P, seqlens=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Skv=100,
+             d=128, scale=0.1, num_splits=0, ws=P, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    st = getattr(fa, fn)(a["q"], a["kq"], a["ks"], a["vq"], a["vs"], a["seqlens"], a["o"], a["lse"],
+                         a["B"], a["Hq"], a["Hkv"], a["Skv"], a["d"], a["scale"], a["num_splits"],
+                         a["ws"], a["ws_bytes"], a["stream"])
+    assert st == want

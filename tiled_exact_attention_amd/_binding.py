@@ -1,10 +1,11 @@
 """ctypes marshalling for libfattn (argument checks and pointers only).
 
-The raw entry points (``fattn_fwd``, ``fattn_decode_int8``,
-``fattn_decode_int4``, ``fattn_kv_append_int8``, ``fattn_kv_append_int4``,
+The raw entry points (``fattn_fwd``, ``fattn_fwd_varlen``, ``fattn_decode_int8``,
+``fattn_decode_int4``, their ``_varlen`` forms, ``fattn_kv_append_int8``,
+``fattn_kv_append_int4``,
 ``fattn_decode_workspace_size``, ``fattn_decode_num_splits``,
 ``fattn_status_string``, ``fattn_version``) have the C names and take plain
-integers (device pointers as ints, streams as ints or None).  ``fwd``,
+integers (device pointers as ints, streams as ints or None).  ``fwd``, ``fwd_varlen``,
 ``decode_int8``, ``decode_int4``, ``kv_append_int8`` and ``kv_append_int4``
 accept torch tensors, allocate the outputs and call them on the current torch
 stream of the tensors' device.
@@ -53,6 +54,12 @@ def load():
         lib.fattn_decode_int8.restype = i32
         lib.fattn_decode_int4.argtypes = lib.fattn_decode_int8.argtypes
         lib.fattn_decode_int4.restype = i32
+        lib.fattn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                         i32, f32, i32, i32, i32, vp]
+        lib.fattn_fwd_varlen.restype = i32
+        for f in (lib.fattn_decode_int8_varlen, lib.fattn_decode_int4_varlen):
+            f.argtypes = [vp] * 8 + [i32] * 5 + [f32, i32, vp, sz, vp]
+            f.restype = i32
         lib.fattn_kv_append_int8.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp]
         lib.fattn_kv_append_int8.restype = i32
         lib.fattn_kv_append_int4.argtypes = lib.fattn_kv_append_int8.argtypes
@@ -80,6 +87,26 @@ def fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, s
                       num_splits, workspace, workspace_bytes, stream) -> int:
     return load().fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d,
                                     scale, num_splits, workspace, workspace_bytes, stream)
+
+
+def fattn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k,
+                     max_seqlen_q, d, scale, causal, window, dtype, stream) -> int:
+    return load().fattn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                                   total_k, max_seqlen_q, d, scale, causal, window, dtype, stream)
+
+
+def fattn_decode_int8_varlen(q, kq, k_scale, vq, v_scale, seqlens, o, lse, B, Hq, Hkv, Skv, d,
+                             scale, num_splits, workspace, workspace_bytes, stream) -> int:
+    return load().fattn_decode_int8_varlen(q, kq, k_scale, vq, v_scale, seqlens, o, lse, B, Hq, Hkv,
+                                           Skv, d, scale, num_splits, workspace, workspace_bytes,
+                                           stream)
+
+
+def fattn_decode_int4_varlen(q, kq, k_scale, vq, v_scale, seqlens, o, lse, B, Hq, Hkv, Skv, d,
+                             scale, num_splits, workspace, workspace_bytes, stream) -> int:
+    return load().fattn_decode_int4_varlen(q, kq, k_scale, vq, v_scale, seqlens, o, lse, B, Hq, Hkv,
+                                           Skv, d, scale, num_splits, workspace, workspace_bytes,
+                                           stream)
 
 
 def fattn_decode_int4(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
@@ -172,6 +199,56 @@ def fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | None =
     return (out, lse) if return_lse else out
 
 
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_seqlen_q: int | None = None,
+               causal: bool = False, window: int = 0, scale: float | None = None,
+               return_lse: bool = False, out=None):
+    """Exact attention over a packed batch of variable-length sequences (see
+    fattn_fwd_varlen).
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d], all float32 or all bfloat16;
+    cu_seqlens_q / cu_seqlens_k: int32 GPU tensors [B+1].  max_seqlen_q: the
+    longest query sequence (computed from cu_seqlens_q with a device sync if
+    None).  Returns o like q (and lse [Hq, total_q] fp32).
+    """
+    import torch
+    dtype = q.dtype
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    _check(q, "q", dtype, 3)
+    _check(k, "k", dtype, 3, q.device)
+    _check(v, "v", dtype, 3, q.device)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, q.device)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1, q.device)
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    if dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    B = cu_seqlens_q.numel() - 1
+    if B < 1 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 offsets, B >= 1")
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max()) if total_q else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", dtype, 3, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if return_lse else None
+    with torch.cuda.device(q.device):
+        st = fattn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if lse is not None else None,
+                              cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv,
+                              total_q, total_k, int(max_seqlen_q), d, float(scale),
+                              int(bool(causal)), int(window),
+                              FATTN_F32 if dtype == torch.float32 else FATTN_BF16, _stream_of(q.device))
+    if st != 0:
+        raise FattnError(st, "fattn_fwd_varlen")
+    return (out, lse) if return_lse else out
+
+
 def decode_num_splits(B, Hq, Hkv, Skv, d, num_splits=0) -> int:
     n = fattn_decode_num_splits(B, Hq, Hkv, Skv, d, num_splits)
     if n < 1:
@@ -186,7 +263,8 @@ def decode_workspace_size(B, Hq, Hkv, Skv, d, num_splits=0) -> int:
     return n
 
 
-def _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, bits):
+def _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, bits,
+            seqlens=None):
     import torch
     _check(q, "q", torch.bfloat16, 3)
     dev = q.device
@@ -216,36 +294,52 @@ def _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_ls
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None
-    fn, name = (fattn_decode_int8, "fattn_decode_int8") if bits == 8 else (fattn_decode_int4, "fattn_decode_int4")
+    lse_p = lse.data_ptr() if lse is not None else None
     with torch.cuda.device(dev):
-        st = fn(q.data_ptr(), kq.data_ptr(), k_scale.data_ptr(), vq.data_ptr(),
-                v_scale.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                B, Hq, Hkv, Skv, d, float(scale), int(num_splits),
-                workspace.data_ptr(), ws_bytes, _stream_of(dev))
+        if seqlens is None:
+            fn, name = (fattn_decode_int8, "fattn_decode_int8") if bits == 8 else \
+                (fattn_decode_int4, "fattn_decode_int4")
+            st = fn(q.data_ptr(), kq.data_ptr(), k_scale.data_ptr(), vq.data_ptr(),
+                    v_scale.data_ptr(), out.data_ptr(), lse_p, B, Hq, Hkv, Skv, d, float(scale),
+                    int(num_splits), workspace.data_ptr(), ws_bytes, _stream_of(dev))
+        else:
+            _check(seqlens, "seqlens", torch.int32, 1, dev)
+            if seqlens.numel() != B:
+                raise ValueError("seqlens must hold B lengths")
+            fn, name = (fattn_decode_int8_varlen, "fattn_decode_int8_varlen") if bits == 8 else \
+                (fattn_decode_int4_varlen, "fattn_decode_int4_varlen")
+            st = fn(q.data_ptr(), kq.data_ptr(), k_scale.data_ptr(), vq.data_ptr(),
+                    v_scale.data_ptr(), seqlens.data_ptr(), out.data_ptr(), lse_p, B, Hq, Hkv, Skv,
+                    d, float(scale), int(num_splits), workspace.data_ptr(), ws_bytes,
+                    _stream_of(dev))
     if st != 0:
         raise FattnError(st, name)
     return (out, lse) if return_lse else out
 
 
 def decode_int8(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_splits: int = 0,
-                workspace=None, return_lse: bool = False, out=None):
+                workspace=None, return_lse: bool = False, out=None, seqlens=None):
     """Decode attention of one token over an int8 KV cache (see fattn_decode_int8).
 
     q [B, Hq, d] bf16; kq/vq [B, Hkv, Skv, d] int8; k_scale/v_scale [B, Hkv, Skv] fp32.
     workspace: optional uint8 GPU tensor of at least decode_workspace_size(...)
-    bytes (allocated here if None).  Returns o [B, Hq, d] bf16 (and lse [B, Hq]).
+    bytes (allocated here if None).  seqlens: optional int32 GPU tensor [B];
+    sequence b then attends to its first seqlens[b] tokens (fattn_decode_int8_varlen).
+    Returns o [B, Hq, d] bf16 (and lse [B, Hq]).
     """
-    return _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, 8)
+    return _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, 8,
+                   seqlens)
 
 
 def decode_int4(q, kq, k_scale, vq, v_scale, *, scale: float | None = None, num_splits: int = 0,
-                workspace=None, return_lse: bool = False, out=None):
+                workspace=None, return_lse: bool = False, out=None, seqlens=None):
     """Decode attention of one token over an int4 KV cache (see fattn_decode_int4).
 
     As decode_int8, with kq/vq [B, Hkv, Skv, d/2] uint8 holding two signed
     4-bit codes per byte (element 2i in the low nibble of byte i).
     """
-    return _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, 4)
+    return _decode(q, kq, k_scale, vq, v_scale, scale, num_splits, workspace, return_lse, out, 4,
+                   seqlens)
 
 
 def _kv_append(x, codes, scales, pos, bits):

@@ -68,6 +68,7 @@ struct SplitParams {
   const float* vs;
   float* part_o;
   float* part_lse;
+  const int* seqlens;  // [B] tokens each sequence sees (first seqlens[b]), or null: all Skv
   int Hq, Hkv, Skv;
   int G;        // query heads per kv head
   int nhc;      // head chunks per kv head: ceil(G / 16)
@@ -167,8 +168,11 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   const float* ksb = p.ks + stream * p.Skv;
   const float* vsb = p.vs + stream * p.Skv;
 
+  // a sequence shorter than the cache leaves its later splits empty (o = 0,
+  // lse = -inf, weight 0 in the merge); lengths are clamped to [0, Skv]
+  const int len = p.seqlens ? min(max(p.seqlens[b], 0), p.Skv) : p.Skv;
   const int t_begin = split * p.chunk;
-  const int t_end = min(p.Skv, t_begin + p.chunk);
+  const int t_end = min(len, t_begin + p.chunk);
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
   // query heads as the B operand.  k-step m covers, for lane group g,
@@ -432,6 +436,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.vs = a.vscale;
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
+  p.seqlens = a.seqlens;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.Skv = a.Skv;

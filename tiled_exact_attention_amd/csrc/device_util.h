@@ -106,4 +106,37 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask));
 }
 
+// Rows and lengths of one sequence: dense batches index b * S; packed batches
+// read the cumulative offsets, clamped so that no value can address memory
+// outside the packed tensors (Sq of a packed batch is the longest query
+// sequence, Skv is unused).
+struct SeqView {
+  int Sq, Skv;
+  int64_t q_row0, k_row0;   // first packed row of the sequence
+  int64_t lse0, lse_hs;     // lse index of (head 0, position 0), head stride
+};
+
+__device__ __forceinline__ SeqView seq_view(const int* cu_q, const int* cu_k, int total_q,
+                                            int total_k, int b, int Hq, int Sq, int Skv) {
+  SeqView s;
+  if (!cu_q) {
+    s.Sq = Sq;
+    s.Skv = Skv;
+    s.q_row0 = int64_t(b) * Sq;
+    s.k_row0 = int64_t(b) * Skv;
+    s.lse0 = int64_t(b) * Hq * Sq;
+    s.lse_hs = Sq;
+    return s;
+  }
+  const int q0 = min(max(cu_q[b], 0), total_q), q1 = min(max(cu_q[b + 1], q0), total_q);
+  const int k0 = min(max(cu_k[b], 0), total_k), k1 = min(max(cu_k[b + 1], k0), total_k);
+  s.Sq = min(q1 - q0, Sq);  // the grid covers Sq (the longest sequence) rows
+  s.Skv = k1 - k0;
+  s.q_row0 = q0;
+  s.k_row0 = k0;
+  s.lse0 = q0;
+  s.lse_hs = total_q;
+  return s;
+}
+
 }  // namespace fattn

@@ -31,6 +31,7 @@ bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 // Kernels use 16-byte vector loads/stores on every tensor.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Automatic split count.  The split kernel runs one wave per (b, kv head,
 // chunk of <= 16 query heads, split) at up to two waves per SIMD, so MI355X
@@ -93,10 +94,11 @@ size_t workspace_bytes_for(int B, int Hq, int nsplit, int d) {
 int decode(const void* q, const void* kq, const float* k_scale, const void* vq,
            const float* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Skv, int d,
            float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream,
-           int bits) {
+           int bits, const int* seqlens = nullptr, bool varlen = false) {
   int st = validate_decode(q, kq, k_scale, vq, v_scale, o, B, Hq, Hkv, Skv, d, scale,
                            num_splits, true);
   if (st != FATTN_OK) return st;
+  if (varlen && (!seqlens || !aligned4(seqlens))) return FATTN_EINVAL;
   int nsplit, chunk;
   plan_splits(B, Hq, Hkv, Skv, num_splits, &nsplit, &chunk);
   size_t need = workspace_bytes_for(B, Hq, nsplit, d);
@@ -107,7 +109,8 @@ int decode(const void* q, const void* kq, const float* k_scale, const void* vq,
   size_t o_bytes = (rows * size_t(d) * sizeof(float) + 255) / 256 * 256;
   fattn::DecodeArgs a{q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
                       nsplit, chunk, static_cast<float*>(workspace),
-                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes), bits};
+                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes), bits,
+                      seqlens};
   hipError_t err = fattn::launch_decode(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
 }
@@ -153,6 +156,35 @@ int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
 }
 
+int fattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                     int total_q, int total_k, int max_seqlen_q, int d, float scale, int causal,
+                     int window, int dtype, void* stream) {
+  // empty tensors may come with null pointers: q/o are only needed when there
+  // are query rows, k/v only when there are keys
+  if (B < 1 || Hq < 1 || Hkv < 1 || total_q < 0 || total_k < 0 || d < 1) return FATTN_EINVAL;
+  if (!cu_seqlens_q || !cu_seqlens_k) return FATTN_EINVAL;
+  if ((total_q > 0 && (!q || !o)) || (total_k > 0 && (!k || !v))) return FATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FATTN_EINVAL;
+  if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k) || (lse && !aligned4(lse))) return FATTN_EINVAL;
+  if (Hq % Hkv != 0) return FATTN_EINVAL;
+  if (max_seqlen_q < 0 || max_seqlen_q > total_q || (total_q > 0 && max_seqlen_q < 1)) return FATTN_EINVAL;
+  if (!std::isfinite(scale)) return FATTN_EINVAL;
+  if (causal != 0 && causal != 1) return FATTN_EINVAL;
+  if (window < 0 || (window > 0 && !causal)) return FATTN_EINVAL;
+  if (!fits(total_q, Hq, d, 1) || !fits(total_k, Hkv, d, 1)) return FATTN_EINVAL;
+  if (int64_t(B) * Hq * ((int64_t(max_seqlen_q) + 3) / 4) > 0x7fffffff) return FATTN_EINVAL;
+  if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
+  if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
+  if (total_q == 0) return FATTN_OK;  // no query rows: nothing to compute
+
+  fattn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q, total_k, d, scale, causal, window,
+                   cu_seqlens_q, cu_seqlens_k, total_q, total_k};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = dtype == FATTN_F32 ? fattn::launch_fwd_f32(a, s) : fattn::launch_fwd_bf16(a, s);
+  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+}
+
 int fattn_decode_num_splits(int B, int Hq, int Hkv, int Skv, int d, int num_splits) {
   int st = validate_decode(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                            B, Hq, Hkv, Skv, d, 1.0f, num_splits, false);
@@ -184,6 +216,24 @@ int fattn_decode_int4(const void* q, const uint8_t* kq, const float* k_scale,
                       void* stream) {
   return decode(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits,
                 workspace, workspace_bytes, stream, 4);
+}
+
+int fattn_decode_int8_varlen(const void* q, const int8_t* kq, const float* k_scale,
+                             const int8_t* vq, const float* v_scale, const int* seqlens, void* o,
+                             float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                             int num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return decode(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits,
+                workspace, workspace_bytes, stream, 8, seqlens, true);
+}
+
+int fattn_decode_int4_varlen(const void* q, const uint8_t* kq, const float* k_scale,
+                             const uint8_t* vq, const float* v_scale, const int* seqlens, void* o,
+                             float* lse, int B, int Hq, int Hkv, int Skv, int d, float scale,
+                             int num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return decode(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits,
+                workspace, workspace_bytes, stream, 4, seqlens, true);
 }
 
 int fattn_kv_append_int8(const void* x, int8_t* codes, float* scales,

@@ -81,6 +81,10 @@ struct Params {
   float c;       // |scale| * log2(e), >= 1e-30
   int negate;    // 1 if scale < 0 (Q sign flipped on load)
   int causal, window;
+  // packed variable-length batch (null: the dense [B, S, H, d] layout)
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
 
 template <int D>
@@ -109,6 +113,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int rows_pos = kBM >> p.gc_shift;     // positions per block
   const int p0 = qb * rows_pos;
   const int hq0 = hk * p.G + chunk * gc;
+  const SeqView sv = seq_view(p.cu_q, p.cu_k, p.total_q, p.total_k, b, p.Hq, p.Sq, p.Skv);
+  const int Sq = sv.Sq, Skv = sv.Skv;
+  if (p0 >= Sq) return;  // a row block past this sequence's end (block-uniform)
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (scalar)
@@ -117,33 +124,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int row = w * 32 + lq;
   const int pos = p0 + (row >> p.gc_shift);
   const int hq = hq0 + (row & (gc - 1));
-  const bool row_ok = pos < p.Sq;
-  const int64_t off = int64_t(p.Skv) - p.Sq;
+  const bool row_ok = pos < Sq;
+  const int64_t off = int64_t(Skv) - Sq;
 
   // ---- key ranges: block band [jb, je); this row's visible keys [row_lo, row_hi)
-  const int bpos_hi = min(p0 + rows_pos - 1, p.Sq - 1);
-  int64_t jb = 0, je = p.Skv;
-  int64_t row_lo = 0, row_hi = p.Skv;
+  const int bpos_hi = min(p0 + rows_pos - 1, Sq - 1);
+  int64_t jb = 0, je = Skv;
+  int64_t row_lo = 0, row_hi = Skv;
   const int wpos_lo = p0 + ((w * 32) >> p.gc_shift);
-  const int wpos_hi = min(p0 + ((w * 32 + 31) >> p.gc_shift), p.Sq - 1);
-  int64_t w_hi_max = p.Skv, w_lo_min = 0;
+  const int wpos_hi = min(p0 + ((w * 32 + 31) >> p.gc_shift), Sq - 1);
+  int64_t w_hi_max = Skv, w_lo_min = 0;
   if (p.causal) {
-    je = min(int64_t(p.Skv), bpos_hi + off + 1);
-    row_hi = min(int64_t(p.Skv), pos + off + 1);
-    w_hi_max = min(int64_t(p.Skv), wpos_hi + off + 1);
+    je = min(int64_t(Skv), bpos_hi + off + 1);
+    row_hi = min(int64_t(Skv), pos + off + 1);
+    w_hi_max = min(int64_t(Skv), wpos_hi + off + 1);
     if (p.window > 0) {
       jb = max(int64_t(0), p0 + off - p.window + 1);
       row_lo = max(int64_t(0), pos + off - p.window + 1);
       w_lo_min = max(int64_t(0), wpos_lo + off - p.window + 1);
     }
   }
-  const bool wave_active = wpos_lo < p.Sq;
+  const bool wave_active = wpos_lo < Sq;
   const int ntiles = je > jb ? int((je - jb + kBN - 1) / kBN) : 0;
 
   // ---- Q rows of this wave as the B operand (k-step m: columns 16m + 8hh .. +7)
   bf16x8 qf[KSTEPS];
   {
-    const __bf16* qrow = p.q + ((int64_t(b) * p.Sq + (row_ok ? pos : 0)) * p.Hq + hq) * D;
+    const __bf16* qrow = p.q + ((sv.q_row0 + (row_ok ? pos : 0)) * p.Hq + hq) * D;
 #pragma unroll
     for (int m = 0; m < KSTEPS; ++m) {
       uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * m + 8 * hh);
@@ -179,8 +186,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // instruction i covers rows 16w + LPI*i + (lane / KCH), lane's physical
   // chunk lane % KCH holds logical chunk (lane % KCH) ^ swz(row).
   const int64_t kv_stride = int64_t(p.Hkv) * D;
-  const __bf16* kbase = p.k + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
-  const __bf16* vbase = p.v + (int64_t(b) * p.Skv * p.Hkv + hk) * D;
+  const __bf16* kbase = p.k + (sv.k_row0 * p.Hkv + hk) * D;
+  const __bf16* vbase = p.v + (sv.k_row0 * p.Hkv + hk) * D;
   int64_t goff[NLD];   // element offset of this lane's source chunk within a tile
   int ld_row[NLD];
 #pragma unroll
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     goff[i] = int64_t(r) * kv_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
   }
   auto issue_loads = [&](int64_t j0, char* stage) __attribute__((always_inline)) {
-    if (j0 + kBN <= p.Skv) {
+    if (j0 + kBN <= Skv) {
       const __bf16* kt = kbase + j0 * kv_stride;
       const __bf16* vt = vbase + j0 * kv_stride;
 #pragma unroll
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       // last tile of the sequence: rows past the end re-read the last row
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int64_t j = min(j0 + ld_row[i], int64_t(p.Skv) - 1);
+        const int64_t j = min(j0 + ld_row[i], int64_t(Skv) - 1);
         const int64_t e = goff[i] + (j - ld_row[i]) * kv_stride;
         char* dst = stage + (16 * w + LPI * i) * ROWB;
         global_to_lds16(kbase + e, dst);
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   };
   int t_lo = 0, t_hi = ntiles;
   {
-    const int64_t hi_min = p.causal ? min(int64_t(p.Skv), p0 + off + 1) : int64_t(p.Skv);
+    const int64_t hi_min = p.causal ? min(int64_t(Skv), p0 + off + 1) : int64_t(Skv);
     const int64_t lo_max = (p.causal && p.window > 0) ? max(int64_t(0), bpos_hi + off - p.window + 1) : 0;
     t_hi = hi_min - jb >= kBN ? int(min(int64_t(ntiles), (hi_min - jb) / kBN)) : 0;
     t_lo = lo_max > jb ? int(min(int64_t(t_hi), (lo_max - jb + kBN - 1) / kBN)) : 0;
@@ -334,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  __bf16* orow = p.o + ((int64_t(b) * p.Sq + pos) * p.Hq + hq) * D;
+  __bf16* orow = p.o + ((sv.q_row0 + pos) * p.Hq + hq) * D;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
@@ -348,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     }
   }
   if (hh == 0 && p.lse) {
-    p.lse[(int64_t(b) * p.Hq + hq) * p.Sq + pos] =
+    p.lse[sv.lse0 + int64_t(hq) * sv.lse_hs + pos] =
         l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
   }
 }
@@ -383,6 +390,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.negate = a.scale < 0.f ? 1 : 0;
   p.causal = a.causal;
   p.window = a.window;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
   const int64_t blocks = int64_t(p.nqb) * p.nx;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.d == 64) {

@@ -10,6 +10,7 @@
 //
 // Arithmetic: fp32 dot products (fma chains in index order), exp via expf on
 // scale * s - m, fp32 accumulation; lse = m + log(l).
+#include "device_util.h"
 #include "launch.h"
 
 #include <cmath>
@@ -28,12 +29,16 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
                                                      float* __restrict__ o,
                                                      float* __restrict__ lse,
                                                      int Hq, int Hkv, int Sq, int Skv,
-                                                     float scale, int causal, int window) {
+                                                     float scale, int causal, int window,
+                                                     const int* __restrict__ cu_q,
+                                                     const int* __restrict__ cu_k,
+                                                     int total_q, int total_k) {
   __shared__ float4 ks[kTile * D / 4];
   __shared__ float4 vs[kTile * D / 4];
 
   const int lane = threadIdx.x;
-  // blockIdx.x enumerates (query block, head, batch), query block fastest
+  // blockIdx.x enumerates (query block, head, batch), query block fastest;
+  // Sq / Skv are the (longest) sequence lengths the grid was sized for
   const int nqb = (Sq + kRows - 1) / kRows;
   const int qblk = int(blockIdx.x % unsigned(nqb));
   const int bh = int(blockIdx.x / unsigned(nqb));
@@ -41,6 +46,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
   const int b = bh / Hq;
   const int hk = h / (Hq / Hkv);
   const int p0 = qblk * kRows;
+  const SeqView sv = seq_view(cu_q, cu_k, total_q, total_k, b, Hq, Sq, Skv);
+  Sq = sv.Sq;
+  Skv = sv.Skv;
+  if (p0 >= Sq) return;  // a row block past this sequence's end (block-uniform)
   const int i = p0 + lane;
   const bool active = i < Sq;
   const int64_t off = int64_t(Skv) - Sq;
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
 
   float qr[D];
   float acc[D];
-  const float* qp = q + ((int64_t(b) * Sq + (active ? i : 0)) * Hq + h) * D;
+  const float* qp = q + ((sv.q_row0 + (active ? i : 0)) * Hq + h) * D;
 #pragma unroll
   for (int c = 0; c < D; c += 4) {
     float4 t = *reinterpret_cast<const float4*>(qp + c);
@@ -75,8 +84,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
   float m = kNegHuge, l = 0.f;
 
   const int64_t kv_row = int64_t(Hkv) * D;  // elements between consecutive keys
-  const float* kb = k + (int64_t(b) * Skv * Hkv + hk) * D;
-  const float* vb = v + (int64_t(b) * Skv * Hkv + hk) * D;
+  const float* kb = k + (sv.k_row0 * Hkv + hk) * D;
+  const float* vb = v + (sv.k_row0 * Hkv + hk) * D;
 
   for (int64_t j0 = blk_lo; j0 < blk_hi; j0 += kTile) {
     __syncthreads();
@@ -136,14 +145,14 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(const float* __restrict__ q
   }
 
   if (!active) return;
-  float* op = o + ((int64_t(b) * Sq + i) * Hq + h) * D;
+  float* op = o + ((sv.q_row0 + i) * Hq + h) * D;
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int c = 0; c < D; c += 4) {
     *reinterpret_cast<float4*>(op + c) =
         make_float4(acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv);
   }
-  if (lse) lse[(int64_t(b) * Hq + h) * Sq + i] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (lse) lse[sv.lse0 + int64_t(h) * sv.lse_hs + i] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
 }  // namespace
@@ -158,10 +167,12 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
   float* o = static_cast<float*>(a.o);
   if (a.d == 64) {
     hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, a.causal, a.window);
+                       a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, a.causal, a.window, a.cu_q, a.cu_k,
+                       a.total_q, a.total_k);
   } else {
     hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, a.causal, a.window);
+                       a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, a.causal, a.window, a.cu_q, a.cu_k,
+                       a.total_q, a.total_k);
   }
   return hipGetLastError();
 }

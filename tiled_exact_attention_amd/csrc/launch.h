@@ -9,6 +9,9 @@ namespace fattn {
 
 // Arguments of one prefill call after validation.  Pointers are device
 // pointers; q/o are [B, Sq, Hq, d], k/v [B, Skv, Hkv, d], lse [B, Hq, Sq] or null.
+// Packed variable-length batches set cu_q / cu_k ([B+1] device offsets): then
+// q/o are [total_q, Hq, d], k/v [total_k, Hkv, d], lse [Hq, total_q], and Sq /
+// Skv are the longest sequence lengths (they size the grid).
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -19,6 +22,10 @@ struct FwdArgs {
   float scale;
   int causal;
   int window;
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0;
+  int total_k = 0;
 };
 
 // Arguments of one quantised-cache decode call after validation and split planning.
@@ -37,6 +44,7 @@ struct DecodeArgs {
   float* part_o;          // workspace: [B, Hq, nsplit, d] fp32
   float* part_lse;        // workspace: [B, Hq, nsplit] fp32
   int bits;               // code width: 8 (int8) or 4 (two int4 codes per byte)
+  const int* seqlens = nullptr;  // [B] device lengths (first seqlens[b] tokens), or null
 };
 
 // Arguments of one KV-cache append after validation.

@@ -74,6 +74,32 @@ INT4_DECODE = Decode("GQA decode over int4 KV cache B32 Hq32 Hkv8 Skv32768 d128"
 PREFILL_WORKLOADS = (TINY_F32, MHA_CAUSAL, GQA_CAUSAL, MQA_CAUSAL, MQA_WINDOW)
 
 
+@dataclasses.dataclass(frozen=True)
+class VarlenPrefill:
+    name: str
+    lens: tuple      # per-sequence lengths (queries = keys: causal self-attention)
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    dtype: str
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# A packed batch of 8 GQA sequences of mixed lengths, 16K tokens in all.
+VARLEN_PREFILL = VarlenPrefill("packed variable-length GQA causal prefill bf16 8 sequences 256..4096 "
+                               "(16384 tokens) Hq32 Hkv8 d128",
+                               (4096, 512, 2048, 1024, 3072, 256, 1792, 3584), 32, 8, 128, True, "bf16", 6)
+# Decode over a 32K-token int8 cache whose 32 sequences hold 1 .. 32768 tokens
+# (uniform, seeded; drawn after the cache).
+VARLEN_DECODE = Decode("GQA decode over int8 KV cache with per-sequence lengths 1..32768 "
+                       "B32 Hq32 Hkv8 capacity 32768 d128", 32, 32, 8, 32768, 128, 7)
+
+
 def _gen(seed: int, device) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -99,6 +125,35 @@ def prefill_inputs(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", seed=0, device="cpu"):
 
 def workload_inputs(w: Prefill, device="cpu"):
     return prefill_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.d, w.dtype, w.seed, device)
+
+
+def cu_seqlens(lens) -> torch.Tensor:
+    """Cumulative offsets [B+1] (int32) of packed sequences of the given lengths."""
+    out = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    out[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    return out
+
+
+def varlen_inputs(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", seed=0, device="cpu"):
+    """Packed q [sum(lens_q), Hq, d], k/v [sum(lens_k), Hkv, d], i.i.d. N(0,1)
+    drawn Q then K then V, and the int32 offsets cu_q, cu_k [B+1] (on the CPU)."""
+    g = _gen(seed, device)
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+    q = torch.randn((tq, Hq, d), generator=g, device=device, dtype=torch.float32)
+    k = torch.randn((tk, Hkv, d), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((tk, Hkv, d), generator=g, device=device, dtype=torch.float32)
+    return _cast(q, dtype), _cast(k, dtype), _cast(v, dtype), cu_seqlens(lens_q), cu_seqlens(lens_k)
+
+
+def varlen_workload_inputs(w: VarlenPrefill, device="cpu"):
+    return varlen_inputs(w.lens, w.lens, w.Hq, w.Hkv, w.d, w.dtype, w.seed, device)
+
+
+def decode_seqlens(w: Decode) -> torch.Tensor:
+    """Per-sequence lengths of a variable-length decode workload: uniform in
+    1 .. Skv from a generator seeded with seed + 1 (int32, on the CPU)."""
+    g = _gen(w.seed + 1, "cpu")
+    return torch.randint(1, w.Skv + 1, (w.B,), generator=g, dtype=torch.int64).to(torch.int32)
 
 
 def quantize_rows_int8(x: torch.Tensor):
