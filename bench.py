@@ -14,7 +14,8 @@ Each kernel call is timed with HIP events recorded on the stream it runs on
 
 After the timed steps, the next rows of the path are timed the same way
 (informational, under "next"): decode over an int4 cache of the decode
-workload's shape, and the int8 / int4 cache append of one 32K-token tensor.
+workload's shape, a packed variable-length prefill, decode with per-sequence
+cache lengths, and the int8 / int4 cache append of one 32K-token tensor.
 
 The CPU baseline times the fp64 oracle on the host on a bounded sample of the
 prefill workload (whole query rows of a few (batch, head) pairs).
@@ -339,6 +340,37 @@ def main():
                                                out=o4), reps=20)
         result["next"]["decode_int4"] = hbm_entry(w4.name, us, decode_bytes(w4))
         del q4, k4, ks4, v4, vs4, o4, ws4
+        torch.cuda.empty_cache()
+
+        # packed variable-length prefill (FLOPs counted per sequence, exactly)
+        wv = W.VARLEN_PREFILL
+        log(f"generating {wv.name}")
+        vq_, vk_, vv_, vcq, vck = (t.to(dev) for t in W.varlen_workload_inputs(wv))
+        vo = torch.empty_like(vq_)
+        us = time_calls(lambda: fa.fwd_varlen(vq_, vk_, vv_, vcq, vck, max_seqlen_q=max(wv.lens),
+                                              causal=wv.causal, scale=wv.scale, out=vo), reps=20)
+        vflops = sum(4 * wv.d * visible_pairs(n, n, wv.causal, 0) * wv.Hq for n in wv.lens)
+        result["next"]["prefill_varlen"] = {
+            "workload": wv.name, "us": round(us, 2),
+            "TFLOP/s": round(vflops / (us * 1e-6) / 1e12, 2),
+            "frac_bf16_peak": round(vflops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop": vflops}
+        del vq_, vk_, vv_, vcq, vck, vo
+
+        # decode with per-sequence lengths (bytes: only the tokens each sequence reads)
+        wl = W.VARLEN_DECODE
+        log(f"generating {wl.name}")
+        lq, lkq, lks, lvq, lvs = W.decode_workload_inputs(wl, device=dev)
+        lens = W.decode_seqlens(wl)
+        lsl = lens.to(dev)
+        lo = torch.empty_like(lq)
+        lws = torch.empty((fa.decode_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.Skv, wl.d, 0),),
+                          dtype=torch.uint8, device=dev)
+        us = time_calls(lambda: fa.decode_int8(lq, lkq, lks, lvq, lvs, scale=wl.scale, workspace=lws,
+                                               out=lo, seqlens=lsl), reps=20)
+        lbytes = int(lens.sum()) * wl.Hkv * (2 * wl.d + 8) + 2 * wl.B * wl.Hq * wl.d * 2
+        result["next"]["decode_int8_varlen"] = hbm_entry(wl.name, us, lbytes)
+        del lq, lkq, lks, lvq, lvs, lo, lws
         torch.cuda.empty_cache()
 
         # KV-cache append: quantise one tensor (K) of the decode workload's 32K-token cache
