@@ -64,6 +64,9 @@ def _load(path: str | None = None):
         lib.oracle_fwd_varlen_rows.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                f64, i32, i32, vp, i64, vp, vp, i32]
         lib.oracle_fwd_varlen_rows.restype = i32
+        lib.oracle_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, i32, i32,
+                                   vp, vp, vp, i32]
+        lib.oracle_bwd.restype = i32
         lib.oracle_max_threads.argtypes = [i32]
         lib.oracle_max_threads.restype = i32
         _libs[path] = lib
@@ -130,6 +133,31 @@ def fwd(q, k, v, *, causal: bool, window: int = 0, scale: float | None = None,
         o = o.reshape(B, Hq, Sq, d).transpose(0, 2, 1, 3).copy()
         lse = lse.reshape(B, Hq, Sq)
     return o, lse
+
+
+def bwd(q, k, v, dout, *, causal: bool, window: int = 0, scale: float | None = None,
+        threads: int = 0, lib: str | None = None):
+    """Gradients (dq, dk, dv) of exact attention for an upstream gradient dout, in fp64.
+
+    q, dout: [B, Sq, Hq, d]; k, v: [B, Skv, Hkv, d].  dk and dv of a kv head sum
+    over the query heads sharing it.  Returns arrays shaped like q, k, v.
+    """
+    qd, kd, vd, dod = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Sq, Hq, d = qd.shape
+    Bk, Skv, Hkv, dk_ = kd.shape
+    if (Bk, dk_) != (B, d) or vd.shape != kd.shape or dod.shape != qd.shape:
+        raise ValueError("shape mismatch between q, k, v and dout")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.empty_like(qd)
+    dk = np.empty_like(kd)
+    dv = np.empty_like(vd)
+    rc = _load(lib).oracle_bwd(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod), B, Hq, Hkv, Sq, Skv, d,
+                               float(scale), int(bool(causal)), int(window),
+                               _ptr(dq), _ptr(dk), _ptr(dv), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_bwd rejected its arguments (code {rc})")
+    return dq, dk, dv
 
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, causal: bool, window: int = 0,

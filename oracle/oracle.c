@@ -421,6 +421,111 @@ int oracle_kv_quantize_int4(const float* x, uint8_t* codes, float* scales,
   return kv_quantize(x, codes, scales, B, Hkv, T, d, pos, cap, 7.0f, 4);
 }
 
+/*
+ * Backward pass: gradients of the forward above with respect to q, k and v,
+ * for an upstream gradient dO of the output ([FA-NPU] recomputation section:
+ * the backward pass recomputes the attention weights instead of storing
+ * them).  Written out from the definition of the forward, per (b, query head
+ * h, query row i), with P_ij the normalised probability of visible key j
+ * (computed here by the same three passes as the forward, not from a saved
+ * lse):
+ *   dV_j  += P_ij dO_i
+ *   dP_ij  = dO_i . V_j
+ *   D_i    = sum_j P_ij dP_ij
+ *   dS_ij  = P_ij (dP_ij - D_i)
+ *   dQ_i   = scale * sum_j dS_ij K_j
+ *   dK_j  += scale * dS_ij Q_i
+ * Masked keys have P_ij = 0 and receive nothing; a row with no visible key
+ * contributes nothing and gets dQ_i = 0.  dK and dV of a kv head sum over the
+ * query heads sharing it.  Layouts as oracle_fwd_rows; dO, dq like q; dk, dv
+ * like k (all double).  One thread owns a (b, kv head) group, so the sums are
+ * taken in a fixed order.
+ */
+int oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
+               int B, int Hq, int Hkv, int Sq, int Skv, int d,
+               double scale, int causal, int window,
+               double* dq, double* dk, double* dv, int nthreads) {
+  if (bad_shape(B, Hq, Hkv, Sq, Skv, d) || window < 0 || (window > 0 && !causal)) return ORACLE_BAD_ARGS;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return ORACLE_BAD_ARGS;
+  int group = Hq / Hkv;
+  int failed = 0;
+  for (int64_t e = 0; e < (int64_t)B * Skv * Hkv * d; e++) {
+    dk[e] = 0.0;
+    dv[e] = 0.0;
+  }
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)Skv);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)Skv);
+    if (!p || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < (int64_t)B * Hkv; bg++) {
+      if (!p || !dp) continue;
+      int64_t b = bg / Hkv, hk = bg % Hkv;
+      int64_t kv_stride = (int64_t)Hkv * d;
+      const double* kh = k + (b * Skv * Hkv + hk) * (int64_t)d;
+      const double* vh = v + (b * Skv * Hkv + hk) * (int64_t)d;
+      double* dkb = dk + (b * Skv * Hkv + hk) * (int64_t)d;
+      double* dvb = dv + (b * Skv * Hkv + hk) * (int64_t)d;
+      for (int64_t h = hk * group; h < (hk + 1) * group; h++) {
+        for (int64_t i = 0; i < Sq; i++) {
+          const double* qi = q + ((b * Sq + i) * Hq + h) * (int64_t)d;
+          const double* dorow = dout + ((b * Sq + i) * Hq + h) * (int64_t)d;
+          double* dqrow = dq + ((b * Sq + i) * Hq + h) * (int64_t)d;
+          int64_t jlo, jhi, j;
+          int c;
+          for (c = 0; c < d; c++) dqrow[c] = 0.0;
+          visible_range(i, Sq, Skv, causal, window, &jlo, &jhi);
+          if (jhi <= jlo) continue;
+          /* P_ij: scores, max, exponentials, normalisation */
+          double m = -INFINITY;
+          for (j = jlo; j < jhi; j++) {
+            double acc = 0.0;
+            for (c = 0; c < d; c++) acc += qi[c] * kh[j * kv_stride + c];
+            p[j - jlo] = scale * acc;
+            if (p[j - jlo] > m) m = p[j - jlo];
+          }
+          double l = 0.0;
+          for (j = jlo; j < jhi; j++) {
+            p[j - jlo] = exp(p[j - jlo] - m);
+            l += p[j - jlo];
+          }
+          for (j = jlo; j < jhi; j++) p[j - jlo] /= l;
+          /* dP_ij and D_i */
+          double D = 0.0;
+          for (j = jlo; j < jhi; j++) {
+            double acc = 0.0;
+            for (c = 0; c < d; c++) acc += dorow[c] * vh[j * kv_stride + c];
+            dp[j - jlo] = acc;
+            D += p[j - jlo] * acc;
+          }
+          /* dV, dS, dQ, dK */
+          for (j = jlo; j < jhi; j++) {
+            double pj = p[j - jlo];
+            double ds = pj * (dp[j - jlo] - D);
+            for (c = 0; c < d; c++) {
+              dvb[j * kv_stride + c] += pj * dorow[c];
+              dqrow[c] += scale * ds * kh[j * kv_stride + c];
+              dkb[j * kv_stride + c] += scale * ds * qi[c];
+            }
+          }
+        }
+      }
+    }
+    free(p);
+    free(dp);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
 /* Number of threads an OpenMP region will use (for reporting). */
 int oracle_max_threads(int nthreads) {
 #ifdef _OPENMP

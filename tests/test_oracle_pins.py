@@ -592,6 +592,67 @@ def pin_decode_seqlens_attend_to_the_prefix(lib):
     assert np.all(o4[1] == 0) and np.all(np.isneginf(l4[1]))
 
 
+def pin_bwd_finite_differences(lib):
+    # L = sum(O * dO) through the (separately pinned) forward oracle; central
+    # differences of L give every element of dq, dk, dv.  GQA, bottom-right causal
+    # with Sq > Skv (two rows see no key), and a window.
+    B, Sq, Skv, Hq, Hkv, d = 1, 5, 4, 4, 2, 3
+    q, k, v = _rand((B, Sq, Hq, d), 67), _rand((B, Skv, Hkv, d), 68), _rand((B, Skv, Hkv, d), 69)
+    do = _rand((B, Sq, Hq, d), 70)
+    for causal, window in ((False, 0), (True, 0), (True, 2)):
+        dq, dk, dv = oracle.bwd(q, k, v, do, causal=causal, window=window, scale=0.8, lib=lib)
+
+        def loss(qq, kk, vv):
+            o, _ = oracle.fwd(qq, kk, vv, causal=causal, window=window, scale=0.8)
+            return float((o * do).sum())
+        eps = 1e-5
+        for x, g, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert np.allclose(g, num, atol=1e-8, rtol=1e-6), (causal, window, which)
+        if causal and Sq > Skv:
+            assert np.all(dq[0, :Sq - Skv] == 0)  # rows with no visible key
+
+
+def pin_bwd_torch_autograd_float64(lib):
+    # an independent library: torch autograd through its float64 math attention,
+    # GQA via repeat_interleave (its backward sums the repeated heads); Sq = Skv.
+    B, S, Hq, Hkv, d = 2, 9, 4, 2, 8
+    q, k, v, do = _rand((B, S, Hq, d), 71), _rand((B, S, Hkv, d), 72), _rand((B, S, Hkv, d), 73), _rand((B, S, Hq, d), 74)
+    for causal in (False, True):
+        dq, dk, dv = oracle.bwd(q, k, v, do, causal=causal, lib=lib)
+        t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3).clone().requires_grad_()
+        tq, tk, tv = t(q), t(k), t(v)
+        rk, rv = tk.repeat_interleave(Hq // Hkv, dim=1), tv.repeat_interleave(Hq // Hkv, dim=1)
+        o = torch.nn.functional.scaled_dot_product_attention(tq, rk, rv, is_causal=causal)
+        (o * torch.from_numpy(do).permute(0, 2, 1, 3)).sum().backward()
+        back = lambda g: g.permute(0, 2, 1, 3).numpy()
+        assert np.allclose(dq, back(tq.grad), atol=1e-12, rtol=0)
+        assert np.allclose(dk, back(tk.grad), atol=1e-12, rtol=0)
+        assert np.allclose(dv, back(tv.grad), atol=1e-12, rtol=0)
+
+
+def pin_bwd_sum_invariants(lib):
+    # each row's probabilities sum to 1 and its dS row sums to 0, so over the keys
+    # of a kv head: sum_j dK_j = 0 and sum_j dV_j = sum of dO over its query rows
+    # that see a key.
+    B, Sq, Skv, Hq, Hkv, d = 2, 7, 9, 6, 3, 5
+    q, k, v = _rand((B, Sq, Hq, d), 75), _rand((B, Skv, Hkv, d), 76), _rand((B, Skv, Hkv, d), 77)
+    do = _rand((B, Sq, Hq, d), 78)
+    for causal, window in ((False, 0), (True, 0), (True, 3)):
+        dq, dk, dv = oracle.bwd(q, k, v, do, causal=causal, window=window, lib=lib)
+        assert np.allclose(dk.sum(axis=1), 0, atol=1e-12)
+        want = do.reshape(B, Sq, Hkv, Hq // Hkv, d).sum(axis=(1, 3))
+        assert np.allclose(dv.sum(axis=1), want, atol=1e-12)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -637,6 +698,11 @@ MUTANTS = {
     "varlen keys of the first sequence": ("const double* kb = k + ((int64_t)cu_k[b] * Hkv + hk) * (int64_t)d;",
                                           "const double* kb = k + ((int64_t)cu_k[0] * Hkv + hk) * (int64_t)d;"),
     "decode ignores seqlens": ("int64_t len = seqlens ? seqlens[b] : Skv;", "int64_t len = Skv;"),
+    "bwd D from unnormalised weights": ("D += p[j - jlo] * acc;", "D += acc;"),
+    "bwd dq without scale": ("dqrow[c] += scale * ds * kh[j * kv_stride + c];", "dqrow[c] += ds * kh[j * kv_stride + c];"),
+    "bwd dS sign flipped": ("double ds = pj * (dp[j - jlo] - D);", "double ds = pj * (D - dp[j - jlo]);"),
+    "bwd dk from k": ("dkb[j * kv_stride + c] += scale * ds * qi[c];", "dkb[j * kv_stride + c] += scale * ds * kh[j * kv_stride + c];"),
+    "bwd dv from q": ("dvb[j * kv_stride + c] += pj * dorow[c];", "dvb[j * kv_stride + c] += pj * qi[c];"),
     "quantiser rounds half away from zero": ("float r = rintf(qv);", "float r = roundf(qv);"),
     "quantiser ignores the append position": ("int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;",
                                              "int64_t slot = (b * Hkv + h) * (int64_t)cap + t;"),
