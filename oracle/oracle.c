@@ -425,21 +425,23 @@ int oracle_kv_quantize_int4(const float* x, uint8_t* codes, float* scales,
  * Backward pass: gradients of the forward above with respect to q, k and v,
  * for an upstream gradient dO of the output ([FA-NPU] recomputation section:
  * the backward pass recomputes the attention weights instead of storing
- * them).  Written out from the definition of the forward, per (b, query head
- * h, query row i), with P_ij the normalised probability of visible key j
- * (computed here by the same three passes as the forward, not from a saved
- * lse):
- *   dV_j  += P_ij dO_i
- *   dP_ij  = dO_i . V_j
- *   D_i    = sum_j P_ij dP_ij
- *   dS_ij  = P_ij (dP_ij - D_i)
- *   dQ_i   = scale * sum_j dS_ij K_j
- *   dK_j  += scale * dS_ij Q_i
+ * them).  Written out from the definition of the forward, with P_ij the
+ * normalised probability of visible key j for query row i of head h:
+ *   dV_j  = sum_i P_ij dO_i
+ *   dP_ij = dO_i . V_j
+ *   D_i   = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij K_j
+ *   dK_j  = scale * sum_i dS_ij Q_i
  * Masked keys have P_ij = 0 and receive nothing; a row with no visible key
  * contributes nothing and gets dQ_i = 0.  dK and dV of a kv head sum over the
  * query heads sharing it.  Layouts as oracle_fwd_rows; dO, dq like q; dk, dv
- * like k (all double).  One thread owns a (b, kv head) group, so the sums are
- * taken in a fixed order.
+ * like k (all double).
+ * Pass 1 (one thread per query row): the row's P by the forward's three
+ * passes, its dP, D_i and dQ_i; it keeps lse_i = m + log(l) and D_i.
+ * Pass 2 (one thread per key of a kv head): P_ij = exp(scale q_i.k_j - lse_i),
+ * the same weights, summed over the group's query rows in order (head, row).
+ * Neither pass depends on the thread count.
  */
 int oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
                int B, int Hq, int Hkv, int Sq, int Skv, int d,
@@ -448,16 +450,22 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
   if (bad_shape(B, Hq, Hkv, Sq, Skv, d) || window < 0 || (window > 0 && !causal)) return ORACLE_BAD_ARGS;
   if (!q || !k || !v || !dout || !dq || !dk || !dv) return ORACLE_BAD_ARGS;
   int group = Hq / Hkv;
-  int failed = 0;
-  for (int64_t e = 0; e < (int64_t)B * Skv * Hkv * d; e++) {
-    dk[e] = 0.0;
-    dv[e] = 0.0;
+  int64_t nrows = (int64_t)B * Hq * Sq;
+  int64_t kv_stride = (int64_t)Hkv * d;
+  double* row_lse = (double*)malloc(sizeof(double) * (size_t)nrows);
+  double* row_d = (double*)malloc(sizeof(double) * (size_t)nrows);
+  if (!row_lse || !row_d) {
+    free(row_lse);
+    free(row_d);
+    return ORACLE_NO_MEMORY;
   }
+  int failed = 0;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
   (void)nthreads;
 #endif
+  /* pass 1: rows (b, h, i) */
 #pragma omp parallel
   {
     double* p = (double*)malloc(sizeof(double) * (size_t)Skv);
@@ -466,63 +474,92 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
 #pragma omp atomic write
       failed = 1;
     }
-#pragma omp for schedule(dynamic, 1)
-    for (int64_t bg = 0; bg < (int64_t)B * Hkv; bg++) {
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; r++) {
       if (!p || !dp) continue;
-      int64_t b = bg / Hkv, hk = bg % Hkv;
-      int64_t kv_stride = (int64_t)Hkv * d;
+      int64_t b = r / ((int64_t)Hq * Sq), h = (r / Sq) % Hq, i = r % Sq;
+      int64_t hk = h / group;
       const double* kh = k + (b * Skv * Hkv + hk) * (int64_t)d;
       const double* vh = v + (b * Skv * Hkv + hk) * (int64_t)d;
-      double* dkb = dk + (b * Skv * Hkv + hk) * (int64_t)d;
-      double* dvb = dv + (b * Skv * Hkv + hk) * (int64_t)d;
-      for (int64_t h = hk * group; h < (hk + 1) * group; h++) {
-        for (int64_t i = 0; i < Sq; i++) {
-          const double* qi = q + ((b * Sq + i) * Hq + h) * (int64_t)d;
-          const double* dorow = dout + ((b * Sq + i) * Hq + h) * (int64_t)d;
-          double* dqrow = dq + ((b * Sq + i) * Hq + h) * (int64_t)d;
-          int64_t jlo, jhi, j;
-          int c;
-          for (c = 0; c < d; c++) dqrow[c] = 0.0;
-          visible_range(i, Sq, Skv, causal, window, &jlo, &jhi);
-          if (jhi <= jlo) continue;
-          /* P_ij: scores, max, exponentials, normalisation */
-          double m = -INFINITY;
-          for (j = jlo; j < jhi; j++) {
-            double acc = 0.0;
-            for (c = 0; c < d; c++) acc += qi[c] * kh[j * kv_stride + c];
-            p[j - jlo] = scale * acc;
-            if (p[j - jlo] > m) m = p[j - jlo];
-          }
-          double l = 0.0;
-          for (j = jlo; j < jhi; j++) {
-            p[j - jlo] = exp(p[j - jlo] - m);
-            l += p[j - jlo];
-          }
-          for (j = jlo; j < jhi; j++) p[j - jlo] /= l;
-          /* dP_ij and D_i */
-          double D = 0.0;
-          for (j = jlo; j < jhi; j++) {
-            double acc = 0.0;
-            for (c = 0; c < d; c++) acc += dorow[c] * vh[j * kv_stride + c];
-            dp[j - jlo] = acc;
-            D += p[j - jlo] * acc;
-          }
-          /* dV, dS, dQ, dK */
-          for (j = jlo; j < jhi; j++) {
-            double pj = p[j - jlo];
-            double ds = pj * (dp[j - jlo] - D);
-            for (c = 0; c < d; c++) {
-              dvb[j * kv_stride + c] += pj * dorow[c];
-              dqrow[c] += scale * ds * kh[j * kv_stride + c];
-              dkb[j * kv_stride + c] += scale * ds * qi[c];
-            }
-          }
-        }
+      const double* qi = q + ((b * Sq + i) * Hq + h) * (int64_t)d;
+      const double* doi = dout + ((b * Sq + i) * Hq + h) * (int64_t)d;
+      double* dqi = dq + ((b * Sq + i) * Hq + h) * (int64_t)d;
+      int64_t jlo, jhi, j;
+      int c;
+      for (c = 0; c < d; c++) dqi[c] = 0.0;
+      visible_range(i, Sq, Skv, causal, window, &jlo, &jhi);
+      if (jhi <= jlo) {
+        row_lse[r] = -INFINITY;
+        row_d[r] = 0.0;
+        continue;
       }
+      double m = -INFINITY;
+      for (j = jlo; j < jhi; j++) {
+        double acc = 0.0;
+        for (c = 0; c < d; c++) acc += qi[c] * kh[j * kv_stride + c];
+        p[j - jlo] = scale * acc;
+        if (p[j - jlo] > m) m = p[j - jlo];
+      }
+      double l = 0.0;
+      for (j = jlo; j < jhi; j++) {
+        p[j - jlo] = exp(p[j - jlo] - m);
+        l += p[j - jlo];
+      }
+      for (j = jlo; j < jhi; j++) p[j - jlo] /= l;
+      double D = 0.0;
+      for (j = jlo; j < jhi; j++) {
+        double acc = 0.0;
+        for (c = 0; c < d; c++) acc += doi[c] * vh[j * kv_stride + c];
+        dp[j - jlo] = acc;
+        D += p[j - jlo] * acc;
+      }
+      for (j = jlo; j < jhi; j++) {
+        double dsq = p[j - jlo] * (dp[j - jlo] - D);
+        for (c = 0; c < d; c++) dqi[c] += scale * dsq * kh[j * kv_stride + c];
+      }
+      row_lse[r] = m + log(l);
+      row_d[r] = D;
     }
     free(p);
     free(dp);
   }
+  /* pass 2: keys (b, kv head, j), summing over the group's rows in order */
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < (int64_t)B * Hkv * Skv; t++) {
+    int64_t b = t / ((int64_t)Hkv * Skv), hk = (t / Skv) % Hkv, j = t % Skv;
+    const double* kj = k + ((b * Skv + j) * Hkv + hk) * (int64_t)d;
+    const double* vj = v + ((b * Skv + j) * Hkv + hk) * (int64_t)d;
+    double* dkj = dk + ((b * Skv + j) * Hkv + hk) * (int64_t)d;
+    double* dvj = dv + ((b * Skv + j) * Hkv + hk) * (int64_t)d;
+    int c;
+    for (c = 0; c < d; c++) {
+      dkj[c] = 0.0;
+      dvj[c] = 0.0;
+    }
+    for (int64_t h = hk * group; h < (hk + 1) * group; h++) {
+      for (int64_t i = 0; i < Sq; i++) {
+        int64_t jlo, jhi;
+        visible_range(i, Sq, Skv, causal, window, &jlo, &jhi);
+        if (j < jlo || j >= jhi) continue;
+        int64_t r = (b * Hq + h) * Sq + i;
+        const double* qi = q + ((b * Sq + i) * Hq + h) * (int64_t)d;
+        const double* doi = dout + ((b * Sq + i) * Hq + h) * (int64_t)d;
+        double s = 0.0, dpij = 0.0;
+        for (c = 0; c < d; c++) {
+          s += qi[c] * kj[c];
+          dpij += doi[c] * vj[c];
+        }
+        double pij = exp(scale * s - row_lse[r]);
+        double dsk = pij * (dpij - row_d[r]);
+        for (c = 0; c < d; c++) {
+          dvj[c] += pij * doi[c];
+          dkj[c] += scale * dsk * qi[c];
+        }
+      }
+    }
+  }
+  free(row_lse);
+  free(row_d);
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
 }
 

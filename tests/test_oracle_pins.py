@@ -699,10 +699,12 @@ MUTANTS = {
                                           "const double* kb = k + ((int64_t)cu_k[0] * Hkv + hk) * (int64_t)d;"),
     "decode ignores seqlens": ("int64_t len = seqlens ? seqlens[b] : Skv;", "int64_t len = Skv;"),
     "bwd D from unnormalised weights": ("D += p[j - jlo] * acc;", "D += acc;"),
-    "bwd dq without scale": ("dqrow[c] += scale * ds * kh[j * kv_stride + c];", "dqrow[c] += ds * kh[j * kv_stride + c];"),
-    "bwd dS sign flipped": ("double ds = pj * (dp[j - jlo] - D);", "double ds = pj * (D - dp[j - jlo]);"),
-    "bwd dk from k": ("dkb[j * kv_stride + c] += scale * ds * qi[c];", "dkb[j * kv_stride + c] += scale * ds * kh[j * kv_stride + c];"),
-    "bwd dv from q": ("dvb[j * kv_stride + c] += pj * dorow[c];", "dvb[j * kv_stride + c] += pj * qi[c];"),
+    "bwd dq without scale": ("dqi[c] += scale * dsq * kh[j * kv_stride + c];", "dqi[c] += dsq * kh[j * kv_stride + c];"),
+    "bwd dS sign flipped in dk": ("double dsk = pij * (dpij - row_d[r]);", "double dsk = pij * (row_d[r] - dpij);"),
+    "bwd dS sign flipped in dq": ("double dsq = p[j - jlo] * (dp[j - jlo] - D);", "double dsq = p[j - jlo] * (D - dp[j - jlo]);"),
+    "bwd weights without lse": ("double pij = exp(scale * s - row_lse[r]);", "double pij = exp(scale * s);"),
+    "bwd dk from k": ("dkj[c] += scale * dsk * qi[c];", "dkj[c] += scale * dsk * kj[c];"),
+    "bwd dv from q": ("dvj[c] += pij * doi[c];", "dvj[c] += pij * qi[c];"),
     "quantiser rounds half away from zero": ("float r = rintf(qv);", "float r = roundf(qv);"),
     "quantiser ignores the append position": ("int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;",
                                              "int64_t slot = (b * Hkv + h) * (int64_t)cap + t;"),
