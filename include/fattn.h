@@ -119,6 +119,39 @@ FATTN_API int fattn_fwd_varlen(const void* q, const void* k, const void* v, void
                      int d, float scale, int causal, int window, int dtype, void* stream);
 
 /*
+ * Backward pass of fattn_fwd (bf16): the gradients dq, dk, dv of the
+ * attention output for an upstream gradient dout, by recomputation ([FA-NPU]
+ * recomputation section: the weights are recomputed from the row statistic
+ * the forward saved, lse, instead of being stored).  With P the forward's
+ * probabilities, D = rowsum(dout * o):
+ *   dv = P^T dout,  dS = P * (dout v^T - D),  dq = scale dS k,  dk = scale dS^T q;
+ * dk and dv of a kv head sum over the query heads sharing it (GQA / MQA).
+ *
+ * q, o, dout, dq  [B, Sq, Hq, d] bf16;  k, v, dk, dv  [B, Skv, Hkv, d] bf16
+ * lse        [B, Hq, Sq] fp32: the forward's lse for the same q, k, v, scale,
+ *            causal and window (o likewise its output)
+ * workspace  device scratch of at least fattn_bwd_workspace_size(B, Hq, Hkv,
+ *            Sq, Skv, d) bytes; contents on entry do not matter, undefined on
+ *            return; concurrent calls need separate workspaces
+ * dtype      FATTN_BF16 only (FATTN_F32 returns FATTN_EUNSUPPORTED)
+ * Other rules and errors as fattn_fwd; FATTN_EWORKSPACE if the workspace is
+ * missing, misaligned or too small.  The result does not depend on
+ * scheduling (no atomics): repeated calls give identical bits.
+ */
+FATTN_API int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv,
+              int B, int Hq, int Hkv, int Sq, int Skv, int d,
+              float scale, int causal, int window, int dtype,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fattn_bwd needs, 0 if the arguments are invalid: two fp32
+ * [B, Hq, Sq] row statistics and, when the query heads of a kv head are split
+ * across blocks (few kv heads, many query heads), fp32 partial dk and dv of
+ * [splits, B, Skv, Hkv, d] each; every part rounded up to 256 bytes.  Host
+ * only; a pure function of its arguments. */
+FATTN_API size_t fattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int d);
+
+/*
  * Decode over an int8 KV cache ([FA-3MOVES] move 3: the cache stays
  * compressed and is used as is).  One new query token per sequence attends
  * to all Skv cached tokens.  The cache holds per (token, kv head) an int8 row

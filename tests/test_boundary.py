@@ -46,7 +46,8 @@ def test_library_is_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
-    assert names == sorted(["fattn_fwd", "fattn_fwd_varlen", "fattn_decode_int8", "fattn_decode_int4",
+    assert names == sorted(["fattn_fwd", "fattn_fwd_varlen", "fattn_bwd", "fattn_bwd_workspace_size",
+                            "fattn_decode_int8", "fattn_decode_int4",
                             "fattn_decode_int8_varlen", "fattn_decode_int4_varlen",
                             "fattn_decode_num_splits", "fattn_decode_workspace_size",
                             "fattn_kv_append_int8", "fattn_kv_append_int4",
@@ -250,3 +251,53 @@ def test_decode_varlen_rejects_before_any_device_work(fn, kw, want):
                          a["B"], a["Hq"], a["Hkv"], a["Skv"], a["d"], a["scale"], a["num_splits"],
                          a["ws"], a["ws_bytes"], a["stream"])
     assert st == want
+
+
+def _bwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Sq=8, Skv=8, d=64,
+             scale=0.1, causal=1, window=0, dtype=1, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return fa.fattn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                        a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["d"], a["scale"], a["causal"],
+                        a["window"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), FATTN_EINVAL), (dict(lse=None), FATTN_EINVAL), (dict(do=None), FATTN_EINVAL),
+    (dict(dq=None), FATTN_EINVAL), (dict(dv=None), FATTN_EINVAL), (dict(o=P + 8), FATTN_EINVAL),
+    (dict(lse=P + 4), FATTN_EINVAL), (dict(Sq=0), FATTN_EINVAL), (dict(Hq=3), FATTN_EINVAL),
+    (dict(scale=math.inf), FATTN_EINVAL), (dict(window=3, causal=0), FATTN_EINVAL),
+    (dict(dtype=0), FATTN_EUNSUPPORTED), (dict(d=96), FATTN_EUNSUPPORTED),
+    (dict(ws=None), FATTN_EWORKSPACE), (dict(ws=P + 8), FATTN_EWORKSPACE), (dict(ws_bytes=16), FATTN_EWORKSPACE),
+])
+def test_bwd_rejects_before_any_device_work(kw, want):
+    assert _bwd(**kw) == want
+
+
+def _bwd_splits(B, Hq, Hkv, Skv):
+    """Query-head splits of the dK/dV grid the header documents: about 1024 blocks."""
+    G = Hq // Hkv
+    blocks = B * Hkv * -(-Skv // 128)
+    want = min(max(-(-1024 // blocks), 1), G)
+    hps = -(-G // want)
+    return -(-G // hps)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Skv,d", [
+    (2, 32, 32, 4096, 4096, 128), (1, 32, 8, 4096, 4096, 128), (1, 232, 1, 2048, 2048, 64),
+    (1, 3, 3, 5, 5, 64), (3, 8, 2, 100, 70, 128)])
+def test_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, d):
+    r256 = lambda n: -(-n // 256) * 256
+    ns = _bwd_splits(B, Hq, Hkv, Skv)
+    want = 2 * r256(B * Hq * Sq * 4) + (2 * r256(ns * B * Skv * Hkv * d * 4) if ns > 1 else 0)
+    assert fa.fattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, d) == want
+
+
+def test_bwd_workspace_size_rejects_bad_arguments():
+    assert fa.fattn_bwd_workspace_size(0, 3, 3, 5, 5, 64) == 0
+    assert fa.fattn_bwd_workspace_size(1, 3, 2, 5, 5, 64) == 0
+    assert fa.fattn_bwd_workspace_size(1, 2, 2, 5, 5, 96) == 0
+    if not _gpu_visible():
+        need = fa.fattn_bwd_workspace_size(1, 4, 2, 8, 8, 64)
+        assert _bwd(ws_bytes=need - 1) == FATTN_EWORKSPACE

@@ -11,15 +11,19 @@ fallback: if the library is not built, every call raises.
     o, lse = fa.decode_int8(q, kq, ks, vq, vs, return_lse=True)
     o = fa.decode_int4(q, k4, ks4, v4, vs4)          # two 4-bit codes per byte
     o = fa.fwd_varlen(q, k, v, cu_q, cu_k, causal=True)  # packed variable-length batch
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True)   # backward by recomputation
 """
 from ._binding import (  # noqa: F401
     FATTN_BF16,
     FATTN_F32,
     FattnError,
+    bwd,
     decode_int4,
     decode_int8,
     decode_num_splits,
     decode_workspace_size,
+    fattn_bwd,
+    fattn_bwd_workspace_size,
     fattn_decode_int4,
     fattn_decode_int4_varlen,
     fattn_decode_int8,

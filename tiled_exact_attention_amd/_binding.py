@@ -1,11 +1,12 @@
 """ctypes marshalling for libfattn (argument checks and pointers only).
 
-The raw entry points (``fattn_fwd``, ``fattn_fwd_varlen``, ``fattn_decode_int8``,
+The raw entry points (``fattn_fwd``, ``fattn_fwd_varlen``, ``fattn_bwd``,
+``fattn_bwd_workspace_size``, ``fattn_decode_int8``,
 ``fattn_decode_int4``, their ``_varlen`` forms, ``fattn_kv_append_int8``,
 ``fattn_kv_append_int4``,
 ``fattn_decode_workspace_size``, ``fattn_decode_num_splits``,
 ``fattn_status_string``, ``fattn_version``) have the C names and take plain
-integers (device pointers as ints, streams as ints or None).  ``fwd``, ``fwd_varlen``,
+integers (device pointers as ints, streams as ints or None).  ``fwd``, ``fwd_varlen``, ``bwd``,
 ``decode_int8``, ``decode_int4``, ``kv_append_int8`` and ``kv_append_int4``
 accept torch tensors, allocate the outputs and call them on the current torch
 stream of the tensors' device.
@@ -54,6 +55,10 @@ def load():
         lib.fattn_decode_int8.restype = i32
         lib.fattn_decode_int4.argtypes = lib.fattn_decode_int8.argtypes
         lib.fattn_decode_int4.restype = i32
+        lib.fattn_bwd.argtypes = [vp] * 9 + [i32] * 6 + [f32, i32, i32, i32, vp, sz, vp]
+        lib.fattn_bwd.restype = i32
+        lib.fattn_bwd_workspace_size.argtypes = [i32] * 6
+        lib.fattn_bwd_workspace_size.restype = sz
         lib.fattn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                          i32, f32, i32, i32, i32, vp]
         lib.fattn_fwd_varlen.restype = i32
@@ -87,6 +92,16 @@ def fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, s
                       num_splits, workspace, workspace_bytes, stream) -> int:
     return load().fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d,
                                     scale, num_splits, workspace, workspace_bytes, stream)
+
+
+def fattn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d, scale, causal, window,
+              dtype, workspace, workspace_bytes, stream) -> int:
+    return load().fattn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d, scale, causal,
+                            window, dtype, workspace, workspace_bytes, stream)
+
+
+def fattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, d) -> int:
+    return load().fattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, d)
 
 
 def fattn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k,
@@ -197,6 +212,52 @@ def fwd(q, k, v, *, causal: bool = False, window: int = 0, scale: float | None =
     if st != 0:
         raise FattnError(st, "fattn_fwd")
     return (out, lse) if return_lse else out
+
+
+def bwd(q, k, v, o, lse, dout, *, causal: bool = False, window: int = 0, scale: float | None = None,
+        workspace=None, out=None):
+    """Gradients (dq, dk, dv) of fwd for an upstream gradient dout (see fattn_bwd).
+
+    q, o, dout [B, Sq, Hq, d] and k, v [B, Skv, Hkv, d] bfloat16, lse [B, Hq, Sq]
+    float32 from fwd(..., return_lse=True) with the same causal / window / scale.
+    workspace: optional uint8 GPU tensor of at least fattn_bwd_workspace_size
+    bytes.  out: optional (dq, dk, dv) tensors to write.  Returns (dq, dk, dv).
+    """
+    import torch
+    _check(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, n, torch.bfloat16, 4, dev)
+    _check(lse, "lse", torch.float32, 3, dev)
+    B, Sq, Hq, d = q.shape
+    Bk, Skv, Hkv, dk_ = k.shape
+    if Bk != B or dk_ != d or tuple(v.shape) != tuple(k.shape) or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, o and dout")
+    if tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be [B, Hq, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, d)
+    if need == 0:
+        raise FattnError(-1, "fattn_bwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check(t, n, torch.bfloat16, 4, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have the shape of {n[1:]}")
+    with torch.cuda.device(dev):
+        st = fattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                       dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq,
+                       Skv, d, float(scale), int(bool(causal)), int(window), FATTN_BF16,
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       _stream_of(dev))
+    if st != 0:
+        raise FattnError(st, "fattn_bwd")
+    return dq, dk, dv
 
 
 def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, max_seqlen_q: int | None = None,

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfattn.so")
-SOURCES = ["fattn_api.cpp", "fwd_f32.hip", "fwd_bf16.hip", "decode_kv.hip", "kv_quant.hip"]
+SOURCES = ["fattn_api.cpp", "fwd_f32.hip", "fwd_bf16.hip", "decode_kv.hip", "kv_quant.hip", "bwd_bf16.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,723 @@
+// Backward pass of bf16 tiled exact attention on the gfx950 matrix cores.
+//
+// Method ([FA-NPU] recomputation section: the backward pass recomputes the
+// attention weights from the row statistics saved by the forward instead of
+// storing them): with the forward's lse, a tile's probabilities are
+// P = exp(scale q.k - lse), recomputed tile by tile, and
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q,
+// the gradients of the forward's definition (D equals rowsum(P * dP) because
+// O = P V).  Nothing of size S x S reaches HBM.
+//
+// Three kernels on the caller's stream:
+//  * bwd_pre_kernel: D and lse * log2(e) per query row into the workspace
+//    (one pass over O and dO; a row with no visible key gets +inf, so its
+//    recomputed probabilities are exactly 0).
+//  * bwd_dq_kernel: the forward's layout (4 waves x 32 query rows, GQA head
+//    chunks, K/V tiles of 64 keys streamed HBM -> LDS by LDS-DMA into the
+//    swizzled layout).  Per tile S^T = K Q^T and dP^T = V dO^T (A = K / V rows
+//    from LDS, B = the wave's Q / dO rows held in registers); dS^T lands in
+//    the B-operand layout; dQ^T += K^T dS^T with K^T from transposed LDS
+//    reads.  No running max: lse is known.
+//  * bwd_dkdv_kernel: 4 waves x 32 keys, K and V rows in registers as B
+//    operands; query tiles of 64 rows (Q, dO, lse, D) stream through LDS for
+//    every query head of (a split of) the kv head's group and every tile that
+//    sees the block's keys.  S = Q K^T and dP = dO V^T put one key per lane,
+//    which is the B layout of dV^T += dO^T P and dK^T += Q^T dS (dO^T / Q^T
+//    from transposed LDS reads).  The sum over query heads stays in
+//    registers; when the grid would be too small (few kv heads, many query
+//    heads: MQA) the group is split across blocks that write fp32 partials,
+//    and bwd_reduce_kernel adds them in split order.  No atomics: the result
+//    does not depend on scheduling.
+// P and dS are rounded to bf16 for their products; accumulation is fp32.
+#include "device_util.h"
+#include "launch.h"
+
+#include <cmath>
+#include <type_traits>
+
+namespace fattn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per dQ block
+constexpr int kBN = 64;           // keys per dQ tile
+constexpr int kBK = 32 * kWaves;  // keys per dK/dV block
+constexpr int kBQ = 64;           // query rows per dK/dV tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* o;
+  const __bf16* dout;
+  const float* lse;
+  __bf16* dq;
+  __bf16* dk;
+  __bf16* dv;
+  float* l2;   // workspace [B, Hq, Sq]: lse * log2(e), +inf for a row with no key
+  float* dd;   // workspace [B, Hq, Sq]: D = rowsum(dO * O)
+  float* part_k;  // workspace [nsplit, B, Skv, Hkv, d] fp32 partial dK (nsplit > 1)
+  float* part_v;  // ... and dV
+  int nsplit;     // query-head splits of a kv head's group in the dK/dV kernel
+  int hps;        // query heads per split
+  int B, Hq, Hkv, Sq, Skv;
+  int G;         // query heads per kv head
+  int gc_shift;  // log2 of the heads per dQ row chunk
+  int nchunk;    // G / GC
+  int nqb;       // dQ row blocks per (b, kv head, head chunk)
+  int nx;        // B * Hkv * nchunk
+  float c;       // |scale| * log2(e), >= 1e-30
+  float scale;   // the signed scale
+  int negate;    // 1 if scale < 0 (Q, or K, sign flipped on load)
+  int causal, window;
+};
+
+// ---------------------------------------------------------------- D and lse2
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int L = D / 8;           // lanes per row, 8 values each
+  constexpr int RPB = 256 / L;       // rows per block
+  const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;  // row = (b, i, h), h fastest
+  const int64_t r = int64_t(blockIdx.x) * RPB + threadIdx.x / L;
+  const int li = threadIdx.x % L;
+  const int64_t rr = r < rows ? r : rows - 1;
+  const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(p.o + rr * D + 8 * li);
+  const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(p.dout + rr * D + 8 * li);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = fmaf(float(o8[e]), float(d8[e]), acc);
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) acc += __shfl_xor(acc, m);
+  if (r >= rows || li != 0) return;
+  const int h = int(r % p.Hq);
+  const int64_t bi = r / p.Hq;
+  const int i = int(bi % p.Sq);
+  const int64_t b = bi / p.Sq;
+  const int64_t idx = (b * p.Hq + h) * p.Sq + i;
+  const float lse = p.lse[idx];
+  p.dd[idx] = acc;
+  p.l2[idx] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+}
+
+// ------------------------------------------------------------------------ dQ
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int KCH = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int ROWB = D * 2;                // bytes per K/V row
+  constexpr int TILE_B = kBN * ROWB;         // bytes of one K (or V) tile
+  constexpr int STAGE_B = 2 * TILE_B;        // K tile then V tile
+  constexpr int LPI = 1024 / ROWB;           // rows filled by one 1 KB LDS-DMA instruction
+  constexpr int NLD = kBN / (kWaves * LPI);  // LDS-DMA instructions per wave per tensor per tile
+  constexpr int KSTEPS = D / 16;             // k-steps of the head-dim products
+  constexpr int NB = D / 32;                 // 32-wide blocks of a row
+  static_assert(NLD * LPI * kWaves == kBN, "tile rows must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_B];
+
+  // ---- block -> (batch, kv head, head chunk, query block); heavy blocks first
+  const int id = blockIdx.x;
+  const int x = id % p.nx;
+  const int slot = id / p.nx;
+  const int qb = p.causal ? p.nqb - 1 - slot : slot;
+  const int chunk = x % p.nchunk;
+  const int hk = (x / p.nchunk) % p.Hkv;
+  const int b = x / (p.nchunk * p.Hkv);
+  const int gc = 1 << p.gc_shift;
+  const int rows_pos = kBM >> p.gc_shift;
+  const int p0 = qb * rows_pos;
+  const int hq0 = hk * p.G + chunk * gc;
+  const int Sq = p.Sq, Skv = p.Skv;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lq = lane & 31;
+  const int hh = lane >> 5;
+  const int row = w * 32 + lq;
+  const int pos = p0 + (row >> p.gc_shift);
+  const int hq = hq0 + (row & (gc - 1));
+  const bool row_ok = pos < Sq;
+  const int64_t off = int64_t(Skv) - Sq;
+
+  // ---- key ranges: block band [jb, je); this row's visible keys [row_lo, row_hi)
+  const int bpos_hi = min(p0 + rows_pos - 1, Sq - 1);
+  int64_t jb = 0, je = Skv;
+  int64_t row_lo = 0, row_hi = Skv;
+  const int wpos_lo = p0 + ((w * 32) >> p.gc_shift);
+  const int wpos_hi = min(p0 + ((w * 32 + 31) >> p.gc_shift), Sq - 1);
+  int64_t w_hi_max = Skv, w_lo_min = 0;
+  if (p.causal) {
+    je = min(int64_t(Skv), bpos_hi + off + 1);
+    row_hi = min(int64_t(Skv), pos + off + 1);
+    w_hi_max = min(int64_t(Skv), wpos_hi + off + 1);
+    if (p.window > 0) {
+      jb = max(int64_t(0), p0 + off - p.window + 1);
+      row_lo = max(int64_t(0), pos + off - p.window + 1);
+      w_lo_min = max(int64_t(0), wpos_lo + off - p.window + 1);
+    }
+  }
+  const bool wave_active = wpos_lo < Sq;
+  const int ntiles = je > jb ? int((je - jb + kBN - 1) / kBN) : 0;
+
+  // ---- Q (sign-flipped for a negative scale) and dO rows as B operands
+  // (k-step m: columns 16m + 8hh .. +7); lse2 and D of this lane's row
+  bf16x8 qf[KSTEPS], df[KSTEPS];
+  {
+    const int64_t ro = ((int64_t(b) * Sq + (row_ok ? pos : 0)) * p.Hq + hq) * D;
+#pragma unroll
+    for (int m = 0; m < KSTEPS; ++m) {
+      uint4 raw = *reinterpret_cast<const uint4*>(p.q + ro + 16 * m + 8 * hh);
+      if (p.negate) {
+        raw.x ^= 0x80008000u; raw.y ^= 0x80008000u; raw.z ^= 0x80008000u; raw.w ^= 0x80008000u;
+      }
+      qf[m] = __builtin_bit_cast(bf16x8, raw);
+      df[m] = *reinterpret_cast<const bf16x8*>(p.dout + ro + 16 * m + 8 * hh);
+    }
+  }
+  const int64_t srow = (int64_t(b) * p.Hq + hq) * Sq + (row_ok ? pos : 0);
+  const float l2 = row_ok ? p.l2[srow] : INFINITY;
+  const float dd = row_ok ? p.dd[srow] : 0.f;
+
+  // ---- LDS read offsets (as the forward): row reads of K and V (A operands
+  // of S^T and dP^T), transposed reads of K (A operand of dQ^T = K^T dS^T)
+  int koff[KSTEPS];
+#pragma unroll
+  for (int m = 0; m < KSTEPS; ++m) koff[m] = lq * ROWB + (((2 * m + hh) ^ swz<D>(lq)) << 4);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int h2 = g16 >> 1, nh = g16 & 1;
+  int toff[NB][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int R = 0; R < 2; ++R) {
+      const int r = 4 * h2 + (s16 >> 2) + 8 * R;
+      const int col = nb * 32 + nh * 16 + 4 * (s16 & 3);
+      toff[nb][R] = r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+    }
+  }
+
+  // ---- LDS-DMA load assignment (as the forward)
+  const int64_t kv_stride = int64_t(p.Hkv) * D;
+  const __bf16* kbase = p.k + (int64_t(b) * Skv * p.Hkv + hk) * D;
+  const __bf16* vbase = p.v + (int64_t(b) * Skv * p.Hkv + hk) * D;
+  int64_t goff[NLD];
+  int ld_row[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int r = 16 * w + LPI * i + lane / KCH;
+    ld_row[i] = r;
+    goff[i] = int64_t(r) * kv_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
+  }
+  auto issue_loads = [&](int64_t j0, char* stage) __attribute__((always_inline)) {
+    if (j0 + kBN <= Skv) {
+      const __bf16* kt = kbase + j0 * kv_stride;
+      const __bf16* vt = vbase + j0 * kv_stride;
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        char* dst = stage + (16 * w + LPI * i) * ROWB;
+        global_to_lds16(kt + goff[i], dst);
+        global_to_lds16(vt + goff[i], dst + TILE_B);
+      }
+    } else {
+      // last tile of the keys: rows past the end re-read the last row
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int64_t j = min(j0 + ld_row[i], int64_t(Skv) - 1);
+        const int64_t e = goff[i] + (j - ld_row[i]) * kv_stride;
+        char* dst = stage + (16 * w + LPI * i) * ROWB;
+        global_to_lds16(kbase + e, dst);
+        global_to_lds16(vbase + e, dst + TILE_B);
+      }
+    }
+  };
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+
+  auto compute = [&](int64_t j0, const char* stage, auto masked) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + koff[m] + kb * 32 * ROWB);
+        s[kb] = mfma32(a, qf[m], s[kb]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + kb * 32 * ROWB);
+        dp[kb] = mfma32(av, df[m], dp[kb]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (decltype(masked)::value) {
+      const int lo = int(max(min(row_lo - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
+      const int hi = int(max(min(row_hi - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kc0 = kb * 32 + 8 * (r >> 2) + (r & 3);
+          if (kc0 < lo || kc0 >= hi) s[kb][r] = -INFINITY;
+        }
+      }
+    }
+    // dS^T = P^T (dP^T - D), P^T = 2^(s c - lse2), in the B layout of K^T dS^T
+    bf16x8 dsf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 8 * (kc & 1) + i;
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r], p.c, -l2));
+        e[i] = pe * (dp[kc >> 1][r] - dd);
+      }
+      dsf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const i16x4 a0 = lds_read_tr16(stage + toff[nb][0] + kc * 16 * ROWB);
+        const i16x4 a1 = lds_read_tr16(stage + toff[nb][1] + kc * 16 * ROWB);
+        acc[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(a0, a1)), dsf[kc], acc[nb]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto step = [&](int t, char* cur, char* nxt, auto masked) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 < ntiles) issue_loads(jb + int64_t(t + 1) * kBN, nxt);
+    const int64_t j0 = jb + int64_t(t) * kBN;
+    if constexpr (decltype(masked)::value) {
+      if (wave_active && j0 < w_hi_max && j0 + kBN > w_lo_min) compute(j0, cur, masked);
+    } else {
+      if (wave_active) compute(j0, cur, masked);
+    }
+  };
+  auto pair = [&](int t, auto masked) __attribute__((always_inline)) {
+    step(t, lds, lds + STAGE_B, masked);
+    if (t + 1 < ntiles) step(t + 1, lds + STAGE_B, lds, masked);
+  };
+  int t_lo = 0, t_hi = ntiles;
+  {
+    const int64_t hi_min = p.causal ? min(int64_t(Skv), p0 + off + 1) : int64_t(Skv);
+    const int64_t lo_max = (p.causal && p.window > 0) ? max(int64_t(0), bpos_hi + off - p.window + 1) : 0;
+    t_hi = hi_min - jb >= kBN ? int(min(int64_t(ntiles), (hi_min - jb) / kBN)) : 0;
+    t_lo = lo_max > jb ? int(min(int64_t(t_hi), (lo_max - jb + kBN - 1) / kBN)) : 0;
+    t_lo = (t_lo + 1) & ~1;
+    t_hi = t_hi > t_lo ? t_lo + ((t_hi - t_lo) & ~1) : t_lo;
+  }
+  if (ntiles > 0) issue_loads(jb, lds);
+  int t = 0;
+  for (; t < t_lo; t += 2) pair(t, std::true_type{});
+  for (; t < t_hi; t += 2) pair(t, std::false_type{});
+  for (; t < ntiles; t += 2) pair(t, std::true_type{});
+
+  // ---- dQ = scale * (K^T dS^T)^T, bf16 (RNE)
+  if (!row_ok) return;
+  __bf16* qrow_out = p.dq + ((int64_t(b) * Sq + pos) * p.Hq + hq) * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 ov;
+      ov[0] = (__bf16)(acc[nb][4 * g + 0] * p.scale);
+      ov[1] = (__bf16)(acc[nb][4 * g + 1] * p.scale);
+      ov[2] = (__bf16)(acc[nb][4 * g + 2] * p.scale);
+      ov[3] = (__bf16)(acc[nb][4 * g + 3] * p.scale);
+      *reinterpret_cast<bf16x4*>(qrow_out + nb * 32 + 8 * g + 4 * hh) = ov;
+    }
+  }
+}
+
+// --------------------------------------------------------------------- dK, dV
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int KCH = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int TILE_B = kBQ * ROWB;            // one Q (or dO) tile
+  constexpr int STAGE_B = 2 * TILE_B + 2 * kBQ * 4;  // Q, dO, lse2[64], D[64]
+  constexpr int LPI = 1024 / ROWB;
+  constexpr int NLD = kBQ / (kWaves * LPI);
+  constexpr int KSTEPS = D / 16;
+  constexpr int NB = D / 32;
+  static_assert(NLD * LPI * kWaves == kBQ, "tile rows must split evenly over the waves");
+  static_assert(STAGE_B % 256 == 0, "stages start on a bank-period boundary");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_B];
+
+  // ---- block -> (batch, kv head, head split, key block); for causal masks
+  // the early key blocks see the most queries, so they come first
+  const int nbh = p.B * p.Hkv * p.nsplit;
+  const int x = blockIdx.x % nbh;
+  const int kbi = blockIdx.x / nbh;
+  const int split = x % p.nsplit;
+  const int hk = (x / p.nsplit) % p.Hkv;
+  const int b = x / (p.nsplit * p.Hkv);
+  const int g0 = split * p.hps;                    // first query head (in the group) of the split
+  const int ng = min(p.hps, p.G - g0);             // heads of this split
+  const int Sq = p.Sq, Skv = p.Skv;
+  const int64_t off = int64_t(Skv) - Sq;
+  const int j0 = kbi * kBK;
+  const int j1 = min(j0 + kBK, Skv);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lq = lane & 31;
+  const int hh = lane >> 5;
+  const int jw = j0 + 32 * w;            // this wave's first key
+  const int jwe = min(jw + 32, Skv);     // ... and one past its last
+  const int key = jw + lq;
+  const bool key_ok = key < Skv;
+
+  // ---- K (sign-flipped for a negative scale) and V rows of this lane's key
+  // as B operands (k-step m: columns 16m + 8hh .. +7)
+  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  {
+    const int64_t ro = ((int64_t(b) * Skv + min(key, Skv - 1)) * p.Hkv + hk) * D;
+#pragma unroll
+    for (int m = 0; m < KSTEPS; ++m) {
+      uint4 raw = *reinterpret_cast<const uint4*>(p.k + ro + 16 * m + 8 * hh);
+      if (p.negate) {
+        raw.x ^= 0x80008000u; raw.y ^= 0x80008000u; raw.z ^= 0x80008000u; raw.w ^= 0x80008000u;
+      }
+      kf[m] = __builtin_bit_cast(bf16x8, raw);
+      vf[m] = *reinterpret_cast<const bf16x8*>(p.v + ro + 16 * m + 8 * hh);
+    }
+  }
+
+  // ---- query rows that see some key of the block: key j is visible to query
+  // i iff j <= i + off (causal) and j > i + off - W (window)
+  int i_lo = 0, i_hi = Sq;
+  if (p.causal) {
+    i_lo = int(max(int64_t(0), int64_t(j0) - off));
+    if (p.window > 0) i_hi = int(min(int64_t(Sq), int64_t(j1) - 1 - off + p.window));
+  }
+  const int tq0 = i_lo / kBQ;
+  const int ntq = i_hi > i_lo ? (i_hi + kBQ - 1) / kBQ - tq0 : 0;
+  const int niter = ng > 0 ? ntq * ng : 0;  // (query head of the split, query tile), head-major
+
+  // ---- LDS offsets: row reads of Q / dO (A operands of S and dP),
+  // transposed reads of dO / Q (A operands of dV^T and dK^T)
+  int koff[KSTEPS];
+#pragma unroll
+  for (int m = 0; m < KSTEPS; ++m) koff[m] = lq * ROWB + (((2 * m + hh) ^ swz<D>(lq)) << 4);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int h2 = g16 >> 1, nh = g16 & 1;
+  int toff[NB][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int R = 0; R < 2; ++R) {
+      const int r = 4 * h2 + (s16 >> 2) + 8 * R;
+      const int col = nb * 32 + nh * 16 + 4 * (s16 & 3);
+      toff[nb][R] = r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+    }
+  }
+
+  // ---- LDS-DMA loads of one (head, query tile): wave w fills rows
+  // 16w .. 16w+15 of the Q and dO tiles; waves 0 and 1 also fetch the 64
+  // lse2 and D values
+  const int64_t q_stride = int64_t(p.Hq) * D;
+  int64_t goff[NLD];
+  int ld_row[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int r = 16 * w + LPI * i + lane / KCH;
+    ld_row[i] = r;
+    goff[i] = int64_t(r) * q_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
+  }
+  auto issue_loads = [&](int it, char* stage) __attribute__((always_inline)) {
+    const int g = g0 + it / ntq;
+    const int i0 = (tq0 + it % ntq) * kBQ;
+    const int hq = hk * p.G + g;
+    const __bf16* qb = p.q + (int64_t(b) * Sq * p.Hq + hq) * D;
+    const __bf16* db = p.dout + (int64_t(b) * Sq * p.Hq + hq) * D;
+    if (i0 + kBQ <= Sq) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        char* dst = stage + (16 * w + LPI * i) * ROWB;
+        global_to_lds16(qb + int64_t(i0) * q_stride + goff[i], dst);
+        global_to_lds16(db + int64_t(i0) * q_stride + goff[i], dst + TILE_B);
+      }
+    } else {
+      // last tile of the queries: rows past the end re-read the last row
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int64_t r = min(int64_t(i0) + ld_row[i], int64_t(Sq) - 1);
+        const int64_t e = goff[i] + (r - ld_row[i]) * q_stride;
+        char* dst = stage + (16 * w + LPI * i) * ROWB;
+        global_to_lds16(qb + e, dst);
+        global_to_lds16(db + e, dst + TILE_B);
+      }
+    }
+    if (w < 2) {
+      const float* src = (w == 0 ? p.l2 : p.dd) + (int64_t(b) * p.Hq + hq) * Sq;
+      global_to_lds4(src + min(i0 + lane, Sq - 1), stage + 2 * TILE_B + w * (kBQ * 4));
+    }
+  };
+
+  f32x16 acck[NB], accv[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    acck[nb] = f32x16{};
+    accv[nb] = f32x16{};
+  }
+
+  // One (head, query tile) for this wave's 32 keys.  Registers r of query
+  // half qh hold query row i0 + 32qh + 8(r/4) + 4hh + r%4 (the C layout of
+  // S = Q K^T with one key per lane).
+  auto compute = [&](int i0, const char* stage, auto masked) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      s[qh] = f32x16{};
+      dp[qh] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + koff[m] + qh * 32 * ROWB);
+        s[qh] = mfma32(a, kf[m], s[qh]);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + qh * 32 * ROWB);
+        dp[qh] = mfma32(ad, vf[m], dp[qh]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (decltype(masked)::value) {
+      // pair (query qi, key) visible iff qi < Sq, key < Skv and the causal /
+      // window rule holds; as bounds on qi: vis_lo <= qi < vis_hi
+      int64_t vis_lo = 0, vis_hi = Sq;
+      if (p.causal) {
+        vis_lo = max(int64_t(0), int64_t(key) - off);
+        if (p.window > 0) vis_hi = min(int64_t(Sq), int64_t(key) - off + p.window);
+      }
+      if (!key_ok) vis_hi = 0;
+      const int lo = int(max(min(vis_lo - i0, int64_t(kBQ)), int64_t(-1))) - 4 * hh;
+      const int hi = int(max(min(vis_hi - i0, int64_t(kBQ)), int64_t(-1))) - 4 * hh;
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qc0 = qh * 32 + 8 * (r >> 2) + (r & 3);
+          if (qc0 < lo || qc0 >= hi) s[qh][r] = -INFINITY;
+        }
+      }
+    }
+    // P = 2^(s c - lse2), dS = P (dP - D), both in the B layout of the
+    // transposed products (k-step kc: registers 8(kc&1) .. +7 of half kc/2)
+    const float* l2s = reinterpret_cast<const float*>(stage + 2 * TILE_B);
+    const float* dds = l2s + kBQ;
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int qh = kc >> 1;
+      float pv[8], sv[8];
+#pragma unroll
+      for (int g4 = 0; g4 < 2; ++g4) {
+        const int rb = 8 * (kc & 1) + 4 * g4;            // first register of 4
+        const int qi = qh * 32 + 8 * (rb >> 2) + 4 * hh;  // its query row in the tile
+        const f32x4 L = *reinterpret_cast<const f32x4*>(l2s + qi);
+        const f32x4 Dv = *reinterpret_cast<const f32x4*>(dds + qi);
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[qh][rb + r4], p.c, -L[r4]));
+          pv[4 * g4 + r4] = pe;
+          sv[4 * g4 + r4] = pe * (dp[qh][rb + r4] - Dv[r4]);
+        }
+      }
+      pf[kc] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      dsf[kc] = to_bf16x8(sv[0], sv[1], sv[2], sv[3], sv[4], sv[5], sv[6], sv[7]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the dO / Q tiles)
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const i16x4 d0 = lds_read_tr16(stage + TILE_B + toff[nb][0] + kc * 16 * ROWB);
+        const i16x4 d1 = lds_read_tr16(stage + TILE_B + toff[nb][1] + kc * 16 * ROWB);
+        accv[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(d0, d1)), pf[kc], accv[nb]);
+        const i16x4 q0 = lds_read_tr16(stage + toff[nb][0] + kc * 16 * ROWB);
+        const i16x4 q1 = lds_read_tr16(stage + toff[nb][1] + kc * 16 * ROWB);
+        acck[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(q0, q1)), dsf[kc], acck[nb]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Whether this wave's keys see any / every query of tile [i0, i0 + 64).
+  auto tile_class = [&](int i0) __attribute__((always_inline)) {
+    // returns 0: nothing visible, 1: some pairs masked, 2: all pairs visible
+    if (jw >= Skv) return 0;
+    const int qe = min(i0 + kBQ, Sq);  // one past the tile's last query
+    if (p.causal) {
+      if (int64_t(jw) > int64_t(qe) - 1 + off) return 0;  // every key after every diagonal
+      if (p.window > 0 && int64_t(jwe) - 1 <= int64_t(i0) + off - p.window) return 0;
+    }
+    bool full = (i0 + kBQ <= Sq) && (jw + 32 <= Skv);
+    if (p.causal) {
+      full = full && int64_t(jwe) - 1 <= int64_t(i0) + off;
+      if (p.window > 0) full = full && int64_t(jw) > int64_t(qe) - 1 + off - p.window;
+    }
+    return full ? 2 : 1;
+  };
+
+  auto step = [&](int it, char* cur, char* nxt) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (it + 1 < niter) issue_loads(it + 1, nxt);
+    const int i0 = (tq0 + it % ntq) * kBQ;
+    const int cls = tile_class(i0);
+    if (cls == 2) {
+      compute(i0, cur, std::false_type{});
+    } else if (cls == 1) {
+      compute(i0, cur, std::true_type{});
+    }
+  };
+  if (niter > 0) issue_loads(0, lds);
+  for (int it = 0; it < niter; it += 2) {
+    step(it, lds, lds + STAGE_B);
+    if (it + 1 < niter) step(it + 1, lds + STAGE_B, lds);
+  }
+
+  // ---- dK = scale * (Q^T dS)^T, dV = (dO^T P)^T: bf16 (RNE), or fp32
+  // partials of this head split
+  if (!key_ok) return;
+  const int64_t ko = ((int64_t(b) * Skv + key) * p.Hkv + hk) * D;
+  if (p.nsplit > 1) {
+    const int64_t po = int64_t(split) * p.B * Skv * p.Hkv * D + ko;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 kv4, vv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv4[e] = acck[nb][4 * g + e] * p.scale;
+          vv4[e] = accv[nb][4 * g + e];
+        }
+        *reinterpret_cast<f32x4*>(p.part_k + po + nb * 32 + 8 * g + 4 * hh) = kv4;
+        *reinterpret_cast<f32x4*>(p.part_v + po + nb * 32 + 8 * g + 4 * hh) = vv4;
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 kv4, vv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kv4[e] = (__bf16)(acck[nb][4 * g + e] * p.scale);
+        vv4[e] = (__bf16)(accv[nb][4 * g + e]);
+      }
+      *reinterpret_cast<bf16x4*>(p.dk + ko + nb * 32 + 8 * g + 4 * hh) = kv4;
+      *reinterpret_cast<bf16x4*>(p.dv + ko + nb * 32 + 8 * g + 4 * hh) = vv4;
+    }
+  }
+}
+
+// Sums the head-split partials of dK and dV in split order -> bf16; 8
+// elements per thread.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int64_t n) {
+  const int64_t e = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (e >= n) return;
+  f32x4 k0{}, k1{}, v0{}, v1{};
+  for (int s = 0; s < p.nsplit; ++s) {
+    const int64_t o = int64_t(s) * n + e;
+    k0 += *reinterpret_cast<const f32x4*>(p.part_k + o);
+    k1 += *reinterpret_cast<const f32x4*>(p.part_k + o + 4);
+    v0 += *reinterpret_cast<const f32x4*>(p.part_v + o);
+    v1 += *reinterpret_cast<const f32x4*>(p.part_v + o + 4);
+  }
+  *reinterpret_cast<bf16x8*>(p.dk + e) = to_bf16x8(k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]);
+  *reinterpret_cast<bf16x8*>(p.dv + e) = to_bf16x8(v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]);
+}
+
+int heads_per_chunk_shift(int G) {
+  int s = 0;
+  while (s < 5 && (G % (2 << s)) == 0) ++s;  // largest power of two <= 32 dividing G
+  return s;
+}
+
+template <int D>
+hipError_t launch_all(const BwdParams& p, int64_t pre_blocks, int64_t dq_blocks, int64_t kv_blocks,
+                      hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(unsigned(pre_blocks)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(unsigned(dq_blocks)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(unsigned(kv_blocks)), dim3(kThreads), 0, stream, p);
+  if (p.nsplit > 1) {
+    const int64_t n = int64_t(p.B) * p.Skv * p.Hkv * D;
+    const int64_t blocks = (n / 8 + 255) / 256;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p, n);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int bwd_head_splits(int B, int Hq, int Hkv, int Skv) {
+  // enough (b, kv head, split, key block) blocks for about four per CU
+  const int64_t G = Hq / Hkv;
+  const int64_t blocks = int64_t(B) * Hkv * ((int64_t(Skv) + kBK - 1) / kBK);
+  int64_t want = (1024 + blocks - 1) / blocks;
+  if (want > G) want = G;
+  if (want < 1) want = 1;
+  const int64_t hps = (G + want - 1) / want;
+  return int((G + hps - 1) / hps);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const __bf16*>(a.q);
+  p.k = static_cast<const __bf16*>(a.k);
+  p.v = static_cast<const __bf16*>(a.v);
+  p.o = static_cast<const __bf16*>(a.o);
+  p.dout = static_cast<const __bf16*>(a.dout);
+  p.lse = a.lse;
+  p.dq = static_cast<__bf16*>(a.dq);
+  p.dk = static_cast<__bf16*>(a.dk);
+  p.dv = static_cast<__bf16*>(a.dv);
+  p.l2 = a.l2;
+  p.dd = a.dd;
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.Sq = a.Sq;
+  p.Skv = a.Skv;
+  p.G = a.Hq / a.Hkv;
+  p.gc_shift = heads_per_chunk_shift(p.G);
+  p.nchunk = p.G >> p.gc_shift;
+  const int rows_pos = kBM >> p.gc_shift;
+  p.nqb = (a.Sq + rows_pos - 1) / rows_pos;
+  p.nx = a.B * a.Hkv * p.nchunk;
+  const float c = std::fabs(a.scale) * kLog2e;
+  p.c = c < 1e-30f ? 1e-30f : c;
+  p.scale = a.scale;
+  p.negate = a.scale < 0.f ? 1 : 0;
+  p.causal = a.causal;
+  p.window = a.window;
+  p.nsplit = bwd_head_splits(a.B, a.Hq, a.Hkv, a.Skv);
+  p.hps = (p.G + p.nsplit - 1) / p.nsplit;
+  p.part_k = a.part_k;
+  p.part_v = a.part_v;
+  if (p.nsplit > 1 && (!p.part_k || !p.part_v)) return hipErrorInvalidValue;
+  const int64_t rows = int64_t(a.B) * a.Sq * a.Hq;
+  const int64_t rpb = 256 / (a.d / 8);
+  const int64_t pre_blocks = (rows + rpb - 1) / rpb;
+  const int64_t dq_blocks = int64_t(p.nqb) * p.nx;
+  const int64_t kv_blocks = int64_t(a.B) * a.Hkv * p.nsplit * ((a.Skv + kBK - 1) / kBK);
+  if (pre_blocks > 0x7fffffff || dq_blocks > 0x7fffffff || kv_blocks > 0x7fffffff)
+    return hipErrorInvalidConfiguration;
+  if (a.d == 64) return launch_all<64>(p, pre_blocks, dq_blocks, kv_blocks, stream);
+  return launch_all<128>(p, pre_blocks, dq_blocks, kv_blocks, stream);
+}
+
+}  // namespace fattn

@@ -106,6 +106,21 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
   return fmaxf(x, __shfl_xor(x, mask));
 }
 
+// LDS swizzle of the bf16 attention kernels' K/V (and Q/dO) tiles, rows of d
+// bf16: chunk c (16 bytes) of tile row r is stored at chunk position
+// c ^ swz(r).  swz is GF(2)-linear in the low four row bits and chosen (by an
+// exhaustive search) so that both read patterns are free of bank conflicts:
+// row reads (16 rows at one chunk, the MFMA A operand) and transposed reads
+// (4 consecutive rows x 4 chunks, ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+  } else {
+    return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+  }
+}
+
 // Rows and lengths of one sequence: dense batches index b * S; packed batches
 // read the cumulative offsets, clamped so that no value can address memory
 // outside the packed tensors (Sq of a packed batch is the longest query

@@ -83,6 +83,22 @@ int validate_decode(const void* q, const void* kq, const void* ks, const void* v
   return FATTN_OK;
 }
 
+// Backward workspace: lse * log2(e) then D, each [B, Hq, Sq] fp32; then, if
+// the dK/dV kernel splits the query heads of a group, fp32 partial dK and dV
+// [nsplit, B, Skv, Hkv, d]; every part rounded up to 256 bytes.
+size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+size_t bwd_stat_bytes(int B, int Hq, int Sq) {
+  return round256(size_t(B) * size_t(Hq) * size_t(Sq) * sizeof(float));
+}
+size_t bwd_part_bytes(int B, int Hq, int Hkv, int Skv, int d) {
+  const int ns = fattn::bwd_head_splits(B, Hq, Hkv, Skv);
+  if (ns <= 1) return 0;
+  return round256(size_t(ns) * size_t(B) * size_t(Skv) * size_t(Hkv) * size_t(d) * sizeof(float));
+}
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int d) {
+  return 2 * bwd_stat_bytes(B, Hq, Sq) + 2 * bwd_part_bytes(B, Hq, Hkv, Skv, d);
+}
+
 size_t workspace_bytes_for(int B, int Hq, int nsplit, int d) {
   // partial outputs [B, Hq, nsplit, d] fp32, then partial lse [B, Hq, nsplit]
   // fp32, the second array starting on a 256-byte boundary.
@@ -182,6 +198,43 @@ int fattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float
                    cu_seqlens_q, cu_seqlens_k, total_q, total_k};
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = dtype == FATTN_F32 ? fattn::launch_fwd_f32(a, s) : fattn::launch_fwd_bf16(a, s);
+  return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
+}
+
+size_t fattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || Hq % Hkv != 0) return 0;
+  if (!fits(B, Hq, Sq, 1) || !fits(B, Skv, Hkv, d) || !supported_head_dim(d)) return 0;
+  return bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, d);
+}
+
+int fattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+              int Skv, int d, float scale, int causal, int window, int dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FATTN_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || d < 1) return FATTN_EINVAL;
+  if (Hq % Hkv != 0) return FATTN_EINVAL;
+  if (!std::isfinite(scale)) return FATTN_EINVAL;
+  if (causal != 0 && causal != 1) return FATTN_EINVAL;
+  if (window < 0 || (window > 0 && !causal)) return FATTN_EINVAL;
+  if (!fits(B, Sq, Hq, d) || !fits(B, Skv, Hkv, d)) return FATTN_EINVAL;
+  if (int64_t(B) * Hq * ((int64_t(Sq) + 3) / 4) > 0x7fffffff) return FATTN_EINVAL;
+  if (int64_t(B) * Hkv * ((int64_t(Skv) + 127) / 128) > 0x7fffffff) return FATTN_EINVAL;
+  if (dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
+  if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, d))
+    return FATTN_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const size_t st = bwd_stat_bytes(B, Hq, Sq), pt = bwd_part_bytes(B, Hq, Hkv, Skv, d);
+  fattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d, scale, causal, window,
+                   reinterpret_cast<float*>(ws), reinterpret_cast<float*>(ws + st),
+                   pt ? reinterpret_cast<float*>(ws + 2 * st) : nullptr,
+                   pt ? reinterpret_cast<float*>(ws + 2 * st + pt) : nullptr};
+  hipError_t err = fattn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
 }
 

@@ -53,19 +53,6 @@ constexpr float kLn2 = 0.693147180559945309f;
 // denominator share m_ref, so the result is the same softmax.
 constexpr float kLazy = 8.f;
 
-// LDS swizzle: chunk c of tile row r is stored at chunk position c ^ swz(r).
-// swz is GF(2)-linear in the low four row bits and chosen so that both read
-// patterns below are free of bank conflicts (16 rows at one chunk for the K
-// reads; 4 consecutive rows x 4 chunks for the transposed V reads).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) {
-    return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
-  } else {
-    return ((r & 1) ? 2 : 0) ^ ((r & 2) ? 4 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
-  }
-}
-
 struct Params {
   const __bf16* q;
   const __bf16* k;

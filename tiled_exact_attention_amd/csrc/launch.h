@@ -57,7 +57,32 @@ struct KvQuantArgs {
   int bits;               // 8: int8 codes, scale absmax/127; 4: packed int4, absmax/7
 };
 
+// Arguments of one backward call after validation (bf16, dense layout).
+struct BwdArgs {
+  const void* q;          // [B, Sq, Hq, d]
+  const void* k;          // [B, Skv, Hkv, d]
+  const void* v;
+  const void* o;          // forward output [B, Sq, Hq, d]
+  const float* lse;       // forward lse [B, Hq, Sq]
+  const void* dout;       // upstream gradient [B, Sq, Hq, d]
+  void* dq;               // [B, Sq, Hq, d]
+  void* dk;               // [B, Skv, Hkv, d]
+  void* dv;
+  int B, Hq, Hkv, Sq, Skv, d;
+  float scale;
+  int causal;
+  int window;
+  float* l2;              // workspace [B, Hq, Sq]
+  float* dd;              // workspace [B, Hq, Sq]
+  float* part_k;          // workspace [nsplit, B, Skv, Hkv, d] (nsplit > 1 only)
+  float* part_v;
+};
+
+// Query-head splits of the dK/dV kernel (1: no partials).
+int bwd_head_splits(int B, int Hq, int Hkv, int Skv);
+
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_quant(const KvQuantArgs& a, hipStream_t stream);
