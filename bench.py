@@ -13,9 +13,10 @@ Each kernel call is timed with HIP events recorded on the stream it runs on
 (torch's current stream, which the binding passes to libfattn).
 
 After the timed steps, the next rows of the path are timed the same way
-(informational, under "next"): decode over an int4 cache of the decode
-workload's shape, a packed variable-length prefill, decode with per-sequence
-cache lengths, and the int8 / int4 cache append of one 32K-token tensor.
+(informational, under "next"): the backward pass of the prefill workload,
+decode over an int4 cache of the decode workload's shape, a packed
+variable-length prefill, decode with per-sequence cache lengths, and the
+int8 / int4 cache append of one 32K-token tensor.
 
 The CPU baseline times the fp64 oracle on the host on a bounded sample of the
 prefill workload (whole query rows of a few (batch, head) pairs).
@@ -341,6 +342,27 @@ def main():
         result["next"]["decode_int4"] = hbm_entry(w4.name, us, decode_bytes(w4))
         del q4, k4, ks4, v4, vs4, o4, ws4
         torch.cuda.empty_cache()
+
+        # backward pass on the prefill workload (FLOPs: 2.5x the forward's, the five
+        # products dV, dP, dS-recompute, dQ, dK counted once each)
+        log("backward on the prefill workload")
+        bdo = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(wp.seed + 100),
+                          device=dev).to(torch.bfloat16)
+        bws = torch.empty((fa.fattn_bwd_workspace_size(wp.B, wp.Hq, wp.Hkv, wp.Sq, wp.Skv, wp.d),),
+                          dtype=torch.uint8, device=dev)
+        bout = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        fa.fattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), wp.B, wp.Hq,
+                     wp.Hkv, wp.Sq, wp.Skv, wp.d, wp.scale, int(wp.causal), wp.window, fa.FATTN_BF16,
+                     stream.cuda_stream)
+        us = time_calls(lambda: fa.bwd(q, k, v, o, lse, bdo, causal=wp.causal, scale=wp.scale,
+                                       workspace=bws, out=bout), reps=10)
+        bflops = 2.5 * prefill_flops(wp)
+        result["next"]["bwd"] = {
+            "workload": f"backward of {wp.name}", "us": round(us, 2),
+            "TFLOP/s": round(bflops / (us * 1e-6) / 1e12, 2),
+            "frac_bf16_peak": round(bflops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop": bflops}
+        del bdo, bws, bout
 
         # packed variable-length prefill (FLOPs counted per sequence, exactly)
         wv = W.VARLEN_PREFILL
