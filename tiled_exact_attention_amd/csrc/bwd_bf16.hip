@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------------ dQ
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int KCH = D / 8;                 // 16-byte chunks per K/V row
   constexpr int ROWB = D * 2;                // bytes per K/V row
   constexpr int TILE_B = kBN * ROWB;         // bytes of one K (or V) tile
@@ -201,34 +201,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int64_t kv_stride = int64_t(p.Hkv) * D;
   const __bf16* kbase = p.k + (int64_t(b) * Skv * p.Hkv + hk) * D;
   const __bf16* vbase = p.v + (int64_t(b) * Skv * p.Hkv + hk) * D;
-  int64_t goff[NLD];
-  int ld_row[NLD];
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int r = 16 * w + LPI * i + lane / KCH;
-    ld_row[i] = r;
-    goff[i] = int64_t(r) * kv_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
-  }
+  // (source offsets are recomputed per tile rather than kept in registers)
   auto issue_loads = [&](int64_t j0, char* stage) __attribute__((always_inline)) {
-    if (j0 + kBN <= Skv) {
-      const __bf16* kt = kbase + j0 * kv_stride;
-      const __bf16* vt = vbase + j0 * kv_stride;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        char* dst = stage + (16 * w + LPI * i) * ROWB;
-        global_to_lds16(kt + goff[i], dst);
-        global_to_lds16(vt + goff[i], dst + TILE_B);
-      }
-    } else {
-      // last tile of the keys: rows past the end re-read the last row
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int64_t j = min(j0 + ld_row[i], int64_t(Skv) - 1);
-        const int64_t e = goff[i] + (j - ld_row[i]) * kv_stride;
-        char* dst = stage + (16 * w + LPI * i) * ROWB;
-        global_to_lds16(kbase + e, dst);
-        global_to_lds16(vbase + e, dst + TILE_B);
-      }
+    for (int i = 0; i < NLD; ++i) {
+      const int r = 16 * w + LPI * i + lane / KCH;
+      // rows past the end of the keys re-read the last row
+      const int64_t j = min(j0 + r, int64_t(Skv) - 1);
+      const int64_t e = j * kv_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
+      char* dst = stage + (16 * w + LPI * i) * ROWB;
+      global_to_lds16(kbase + e, dst);
+      global_to_lds16(vbase + e, dst + TILE_B);
     }
   };
 
@@ -236,19 +219,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
 
+  // Order chosen for register pressure (two waves per SIMD): S^T, then P^T
+  // packed to bf16 (the scores die), then dP^T, then dS^T.
   auto compute = [&](int64_t j0, const char* stage, auto masked) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2], dp[2];
+    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      dp[kb] = f32x16{};
 #pragma unroll
       for (int m = 0; m < KSTEPS; ++m) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + koff[m] + kb * 32 * ROWB);
         s[kb] = mfma32(a, qf[m], s[kb]);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + kb * 32 * ROWB);
-        dp[kb] = mfma32(av, df[m], dp[kb]);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -264,17 +246,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         }
       }
     }
-    // dS^T = P^T (dP^T - D), P^T = 2^(s c - lse2), in the B layout of K^T dS^T
+    // P^T = 2^(s c - lse2) as bf16, in the B layout of K^T dS^T
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -l2));
+      pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    }
+    // dP^T = V dO^T, then dS^T = P^T (dP^T - D)
+    __builtin_amdgcn_s_setprio(1);
+    f32x16 dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + kb * 32 * ROWB);
+        dp[kb] = mfma32(av, df[m], dp[kb]);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 dsf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 8 * (kc & 1) + i;
-        const float pe = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][r], p.c, -l2));
-        e[i] = pe * (dp[kc >> 1][r] - dd);
-      }
+      for (int i = 0; i < 8; ++i) e[i] = float(pf[kc][i]) * (dp[kc >> 1][8 * (kc & 1) + i] - dd);
       dsf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
     __builtin_amdgcn_s_setprio(1);
