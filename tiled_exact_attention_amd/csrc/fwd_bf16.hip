@@ -20,16 +20,21 @@
 //    the softmax row statistics need one cross-lane step (lane ^ 32).
 //  * V^T is read from a row-major V tile with ds_read_b64_tr_b16, the
 //    transposing LDS read, in the key order the P layout dictates.
-//  * K/V tiles of 64 keys are double-buffered in LDS and filled straight
-//    from HBM by global_load_lds_dwordx4 (no register staging): the next
-//    tile streams in while the current one is computed.  LDS rows are
-//    XOR-swizzled in 16-byte chunks so neither read pattern has bank
-//    conflicts; each lane's LDS read
-//    offsets are computed once, the stage and block offsets are immediates.
+//  * K/V tiles of 64 keys are filled straight from HBM into LDS by
+//    global_load_lds_dwordx4 (no register staging), two K and two V buffers.
+//    Each wave is software-pipelined by one tile: iteration t multiplies
+//    S(t) = K(t) Q^T and O += V(t-1)^T P(t-1) in one block of matrix
+//    products, then turns S(t) into P(t).  The products of one iteration are
+//    independent, so they are issued as interleaved chains with their LDS
+//    operand reads running a few products ahead; the softmax of one wave
+//    overlaps the products of the other wave on its SIMD.  K(t+1) and V(t)
+//    stream in during iteration t.  LDS rows are XOR-swizzled in 16-byte
+//    chunks so neither read pattern has bank conflicts; each lane's LDS read
+//    offsets are computed once, the buffer and block offsets are immediates.
 //  * causal/window: blocks visit only key tiles that intersect their visible
-//    band; waves skip tiles with no visible key for their rows; the mask is
-//    applied only on tiles that straddle a band edge.  Heavy (late) query
-//    blocks are dispatched first.
+//    band; the mask is applied only on tiles that straddle a band edge (keys
+//    a row cannot see get probability exactly 0).  Heavy (late) query blocks
+//    are dispatched first.
 //  * softmax in base 2 with the scale folded in: p = 2^(s*c - m), c =
 //    scale*log2(e); a negative scale is applied as an exact sign flip of Q.
 #include "device_util.h"
@@ -52,6 +57,23 @@ constexpr float kLn2 = 0.693147180559945309f;
 // more than kLazy; probabilities are then at most 2^kLazy.  Numerator and
 // denominator share m_ref, so the result is the same softmax.
 constexpr float kLazy = 8.f;
+// LDS operand reads are issued this many matrix products ahead of their use.
+constexpr int kLA = 3;
+
+// sched_group_barrier sequences: N instructions of class M (0x008 matrix
+// product, 0x100 LDS read), or REP repetitions of (N1 of M1, N2 of M2).
+template <int M, int N>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(M, N, 0);
+}
+template <int M1, int N1, int M2, int N2, int REP>
+__device__ __forceinline__ void sched_pairs() {
+  if constexpr (REP > 0) {
+    __builtin_amdgcn_sched_group_barrier(M1, N1, 0);
+    __builtin_amdgcn_sched_group_barrier(M2, N2, 0);
+    sched_pairs<M1, N1, M2, N2, REP - 1>();
+  }
+}
 
 struct Params {
   const __bf16* q;
@@ -79,14 +101,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   constexpr int KCH = D / 8;                 // 16-byte chunks per K/V row
   constexpr int ROWB = D * 2;                // bytes per K/V row
   constexpr int TILE_B = kBN * ROWB;         // bytes of one K (or V) tile
-  constexpr int STAGE_B = 2 * TILE_B;        // K tile then V tile
   constexpr int LPI = 1024 / ROWB;           // rows filled by one 1 KB LDS-DMA instruction
   constexpr int NLD = kBN / (kWaves * LPI);  // LDS-DMA instructions per wave per tensor per tile
   constexpr int KSTEPS = D / 16;             // k-steps of the QK^T product
   constexpr int NB = D / 32;                 // 32-wide blocks of the output row
   static_assert(NLD * LPI * kWaves == kBN, "tile rows must split evenly over the waves");
-  static_assert(STAGE_B + TILE_B + (kBN / 2) * ROWB <= 65536 + STAGE_B, "offsets fit");
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE_B];
+  static_assert(4 * TILE_B <= 65536, "LDS read offsets fit the 16-bit immediate");
+  // LDS: K buffers 0 and 1, then V buffers 0 and 1
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_B];
 
   // ---- block -> (batch, kv head, head chunk, query block); heavy blocks first.
   // Workgroups go to the 8 XCDs round-robin (id % 8).  Dense batches number
@@ -133,21 +155,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // ---- key ranges: block band [jb, je); this row's visible keys [row_lo, row_hi)
   const int bpos_hi = min(p0 + rows_pos - 1, Sq - 1);
   int64_t jb = 0, je = Skv;
-  int64_t row_lo = 0, row_hi = Skv;
-  const int wpos_lo = p0 + ((w * 32) >> p.gc_shift);
-  const int wpos_hi = min(p0 + ((w * 32 + 31) >> p.gc_shift), Sq - 1);
-  int64_t w_hi_max = Skv, w_lo_min = 0;
+  int row_lo = 0, row_hi = Skv;
   if (p.causal) {
     je = min(int64_t(Skv), bpos_hi + off + 1);
-    row_hi = min(int64_t(Skv), pos + off + 1);
-    w_hi_max = min(int64_t(Skv), wpos_hi + off + 1);
+    row_hi = int(min(int64_t(Skv), pos + off + 1));
     if (p.window > 0) {
       jb = max(int64_t(0), p0 + off - p.window + 1);
-      row_lo = max(int64_t(0), pos + off - p.window + 1);
-      w_lo_min = max(int64_t(0), wpos_lo + off - p.window + 1);
+      row_lo = int(max(int64_t(0), pos + off - p.window + 1));
     }
   }
-  const bool wave_active = wpos_lo < Sq;
   const int ntiles = je > jb ? int((je - jb + kBN - 1) / kBN) : 0;
 
   // ---- Q rows of this wave as the B operand (k-step m: columns 16m + 8hh .. +7)
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     for (int R = 0; R < 2; ++R) {
       const int r = 4 * h2 + (s16 >> 2) + 8 * R;
       const int col = nb * 32 + nh * 16 + 4 * (s16 & 3);
-      voff[nb][R] = TILE_B + r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
+      voff[nb][R] = r * ROWB + (((col >> 3) ^ swz<D>(r)) << 4) + (col & 7) * 2;
     }
   }
 
@@ -191,33 +207,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int64_t kv_stride = int64_t(p.Hkv) * D;
   const __bf16* kbase = p.k + (sv.k_row0 * p.Hkv + hk) * D;
   const __bf16* vbase = p.v + (sv.k_row0 * p.Hkv + hk) * D;
-  int64_t goff[NLD];   // element offset of this lane's source chunk within a tile
-  int ld_row[NLD];
+  // element offset of this lane's source chunk within a tile (|offset| <
+  // 64 rows of Hkv * d elements, checked on the host to fit 32 bits)
+  int goff[NLD];
+  const int lr = lane / KCH;
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int r = 16 * w + LPI * i + lane / KCH;
-    ld_row[i] = r;
-    goff[i] = int64_t(r) * kv_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
+    goff[i] = r * int(kv_stride) + ((lane % KCH) ^ swz<D>(r)) * 8;
   }
-  auto issue_loads = [&](int64_t j0, char* stage) __attribute__((always_inline)) {
+  // copy rows j0 .. j0+63 of one tensor (K or V) into an LDS buffer; on the
+  // last tile of the sequence, rows past the end re-read the last row
+  auto issue_tile = [&](const __bf16* base, int64_t j0, char* dst_tile) __attribute__((always_inline)) {
     if (j0 + kBN <= Skv) {
-      const __bf16* kt = kbase + j0 * kv_stride;
-      const __bf16* vt = vbase + j0 * kv_stride;
+      const __bf16* src = base + j0 * kv_stride;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        char* dst = stage + (16 * w + LPI * i) * ROWB;
-        global_to_lds16(kt + goff[i], dst);
-        global_to_lds16(vt + goff[i], dst + TILE_B);
-      }
+      for (int i = 0; i < NLD; ++i) global_to_lds16(src + goff[i], dst_tile + (16 * w + LPI * i) * ROWB);
     } else {
-      // last tile of the sequence: rows past the end re-read the last row
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int64_t j = min(j0 + ld_row[i], int64_t(Skv) - 1);
-        const int64_t e = goff[i] + (j - ld_row[i]) * kv_stride;
-        char* dst = stage + (16 * w + LPI * i) * ROWB;
-        global_to_lds16(kbase + e, dst);
-        global_to_lds16(vbase + e, dst + TILE_B);
+        const int row = 16 * w + LPI * i + lr;
+        const int64_t j = min(j0 + row, int64_t(Skv) - 1);
+        global_to_lds16(base + goff[i] + (j - row) * kv_stride, dst_tile + (16 * w + LPI * i) * ROWB);
       }
     }
   };
@@ -227,30 +238,76 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
   float m_run = kNegHuge, l_run = 0.f;
 
-  auto compute = [&](int64_t j0, const char* stage, auto masked) __attribute__((always_inline)) {
-    // S^T = K Q^T for two 32-key blocks.  Matrix-product runs are issued at
-    // raised wave priority so that, of the two waves sharing a SIMD, the one
-    // streaming products keeps the matrix pipe fed while the other one's
-    // softmax fills the vector ALU.
-    __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2];
+  f32x16 s[2];   // S^T of the current tile (two 32-key blocks)
+  bf16x8 pf[4];  // P of the previous tile, the B operand of O^T += V^T P^T
+
+  // ---- one block of matrix products: S(t) = K(t) Q^T (if QK) and
+  // O^T += V(t-1)^T P(t-1)^T (if PV).  The products are issued as
+  // interleaved accumulation chains; the LDS operand reads are placed kLA
+  // products ahead of their use (sched_group_barrier: 0x100 = LDS read,
+  // 0x008 = matrix product).
+  auto products = [&](const char* kt, const char* vt, auto QK, auto PV) __attribute__((always_inline)) {
+    constexpr bool qk = decltype(QK)::value, pv = decltype(PV)::value;
+    constexpr int NQK = 2 * KSTEPS, NPV = 4 * NB;  // products; K reads = NQK, V^T reads = 2 * NPV
+    // A distinct marker per variant keeps the compiler from hoisting the
+    // operand reads the variants share above the branch that selects them
+    // (which would hold all of them in registers at once).
+    if constexpr (qk && pv) {
+      asm volatile("; products: S and PV" ::: "memory");
+    } else if constexpr (qk) {
+      asm volatile("; products: S" ::: "memory");
+    } else {
+      asm volatile("; products: PV" ::: "memory");
+    }
+    if constexpr (qk) {
+      bf16x8 ka[KSTEPS][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      for (int m = 0; m < KSTEPS; ++m)
 #pragma unroll
-      for (int m = 0; m < KSTEPS; ++m) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + koff[m] + kb * 32 * ROWB);
-        s[kb] = mfma32(a, qf[m], s[kb]);
+        for (int kb = 0; kb < 2; ++kb) ka[m][kb] = *reinterpret_cast<const bf16x8*>(kt + koff[m] + kb * 32 * ROWB);
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[m][kb], qf[m], s[kb]);
+    }
+    if constexpr (pv) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const i16x4 a0 = lds_read_tr16(vt + voff[nb][0] + kc * 16 * ROWB);
+          const i16x4 a1 = lds_read_tr16(vt + voff[nb][1] + kc * 16 * ROWB);
+          acc[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(a0, a1)), pf[kc], acc[nb]);
+        }
       }
     }
+    if constexpr (qk && pv) {
+      sched_group<0x100, 2 * kLA>();
+      sched_pairs<0x008, 1, 0x100, 1, NQK>();
+      sched_pairs<0x008, 1, 0x100, 2, NPV - kLA>();
+      sched_group<0x008, kLA>();
+    } else if constexpr (qk) {
+      sched_group<0x100, 2 * kLA>();
+      sched_pairs<0x008, 1, 0x100, 1, NQK - 2 * kLA>();
+      sched_group<0x008, 2 * kLA>();
+    } else if constexpr (pv) {
+      sched_group<0x100, 2 * kLA>();
+      sched_pairs<0x008, 1, 0x100, 2, NPV - kLA>();
+      sched_group<0x008, kLA>();
+    }
+  };
 
-    __builtin_amdgcn_s_setprio(0);
-    // mask (only on tiles that straddle an edge of this wave's band): key
-    // j0 + kofs is visible iff row_lo <= key < row_hi; kofs - 4*hh is a
+  // ---- S(t) -> P(t): mask (only on tiles that straddle an edge of this
+  // wave's band), online softmax in base 2 with the scale folded into c.
+  auto softmax = [&](int64_t j0, auto masked) __attribute__((always_inline)) {
+    // key j0 + kofs is visible iff row_lo <= key < row_hi; kofs - 4*hh is a
     // compile-time constant per register, so compare against shifted bounds.
     if constexpr (decltype(masked)::value) {
-      const int lo = int(max(min(row_lo - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
-      const int hi = int(max(min(row_hi - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
+      const int jj = int(j0);  // j0 < Skv fits an int
+      const int lo = max(min(row_lo - jj, kBN), -1) - 4 * hh;
+      const int hi = max(min(row_hi - jj, kBN), -1) - 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -260,8 +317,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         }
       }
     }
-
-    // online softmax (base 2, scale folded into c)
     float mx = kNegHuge;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -277,8 +332,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
     }
-
-    bf16x8 pf[4];
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       float e[8];
@@ -289,56 +342,67 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       }
       pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
-
-    // O^T += V^T P^T; V^T via transposed LDS reads in the key order of pf
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const i16x4 a0 = lds_read_tr16(stage + voff[nb][0] + kc * 16 * ROWB);
-        const i16x4 a1 = lds_read_tr16(stage + voff[nb][1] + kc * 16 * ROWB);
-        acc[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(a0, a1)), pf[kc], acc[nb]);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- main loop: tile t lives in stage t % 2; tile t+1 streams into the
-  // other stage (HBM -> LDS, no registers) while tile t is computed.
-  // Tiles [t_lo, t_hi) are fully visible to every row of the block and use
-  // the unmasked path; tiles before (window edge) and after (causal edge, end
-  // of the keys) use the masked path, where waves also skip tiles they cannot
-  // see.  Both bounds are even so each stage offset is a compile-time constant.
-  auto step = [&](int t, char* cur, char* nxt, auto masked) __attribute__((always_inline)) {
-    wait_vmcnt<0>();   // this wave's copies of tile t have landed
-    __syncthreads();   // ... and everyone's; everyone is also done with tile t-1
-    if (t + 1 < ntiles) issue_loads(jb + int64_t(t + 1) * kBN, nxt);
+  // ---- main loop.  Iteration t (0 <= t <= ntiles): K(t) and V(t-1) are in
+  // LDS (K buffer t % 2, V buffer (t-1) % 2); K(t+1) and V(t) are copied
+  // into the other buffers meanwhile.  Every buffer a copy overwrites was
+  // last read in iteration t-1, which all waves have left at the barrier.
+  // Iteration 0 forms S(0) only, iteration ntiles only adds V(ntiles-1)^T
+  // P(ntiles-1)^T; every other one does both, so the steady state has no
+  // branches.  Every wave takes every tile of the block's band: keys a row
+  // cannot see get probability exactly 0.  Tiles [t_lo, t_hi) are fully
+  // visible to every row of the block and skip the mask; tile 0, the tiles
+  // before t_lo (window edge) and from t_hi on (causal edge, end of the
+  // keys) are masked.  Iterations run in pairs (odd t, then even t) so the
+  // buffer offsets are compile-time constants.
+  auto begin = [&](int t, char* knxt, char* vcur) __attribute__((always_inline)) {
+    wait_vmcnt<0>();   // this wave's copies of K(t) and V(t-1) have landed
+    __syncthreads();   // ... and everyone's; everyone has left iteration t-1
     const int64_t j0 = jb + int64_t(t) * kBN;
-    if constexpr (decltype(masked)::value) {
-      if (wave_active && j0 < w_hi_max && j0 + kBN > w_lo_min) compute(j0, cur, masked);
-    } else {
-      if (wave_active) compute(j0, cur, masked);
-    }
+    if (t + 1 < ntiles) issue_tile(kbase, j0 + kBN, knxt);
+    if (t < ntiles) issue_tile(vbase, j0, vcur);
+    return j0;
+  };
+  auto iteration = [&](int t, auto odd, auto masked) __attribute__((always_inline)) {
+    constexpr int cur = decltype(odd)::value ? 1 : 0;
+    const int64_t j0 = begin(t, lds + (cur ^ 1) * TILE_B, lds + (2 + cur) * TILE_B);
+    products(lds + cur * TILE_B, lds + (2 + (cur ^ 1)) * TILE_B, std::true_type{}, std::true_type{});
+    softmax(j0, masked);
   };
   auto pair = [&](int t, auto masked) __attribute__((always_inline)) {
-    step(t, lds, lds + STAGE_B, masked);
-    if (t + 1 < ntiles) step(t + 1, lds + STAGE_B, lds, masked);
+    iteration(t, std::true_type{}, masked);
+    if (t + 1 < ntiles) iteration(t + 1, std::false_type{}, masked);
   };
-  int t_lo = 0, t_hi = ntiles;
-  {
-    const int64_t hi_min = p.causal ? min(int64_t(Skv), p0 + off + 1) : int64_t(Skv);
-    const int64_t lo_max = (p.causal && p.window > 0) ? max(int64_t(0), bpos_hi + off - p.window + 1) : 0;
-    t_hi = hi_min - jb >= kBN ? int(min(int64_t(ntiles), (hi_min - jb) / kBN)) : 0;
-    t_lo = lo_max > jb ? int(min(int64_t(t_hi), (lo_max - jb + kBN - 1) / kBN)) : 0;
-    t_lo = (t_lo + 1) & ~1;
-    t_hi = t_hi > t_lo ? t_lo + ((t_hi - t_lo) & ~1) : t_lo;
+  if (ntiles > 0) {
+    int t_lo, t_hi;  // odd, t_lo <= t_hi, t_hi - t_lo even
+    {
+      const int64_t hi_min = p.causal ? min(int64_t(Skv), p0 + off + 1) : int64_t(Skv);
+      const int64_t lo_max = (p.causal && p.window > 0) ? max(int64_t(0), bpos_hi + off - p.window + 1) : 0;
+      const int raw_hi = hi_min - jb >= kBN ? int(min(int64_t(ntiles), (hi_min - jb) / kBN)) : 0;
+      const int raw_lo = lo_max > jb ? int(min(int64_t(raw_hi), (lo_max - jb + kBN - 1) / kBN)) : 0;
+      t_lo = max(raw_lo, 1) | 1;
+      t_hi = raw_hi > t_lo ? t_lo + ((raw_hi - t_lo) & ~1) : t_lo;
+    }
+    issue_tile(kbase, jb, lds);
+    {
+      const int64_t j0 = begin(0, lds + TILE_B, lds + 2 * TILE_B);
+      products(lds, lds, std::true_type{}, std::false_type{});
+      softmax(j0, std::true_type{});
+    }
+    int t = 1;
+    for (; t < t_lo && t < ntiles; t += 2) pair(t, std::true_type{});
+    for (; t < t_hi; t += 2) pair(t, std::false_type{});
+    for (; t < ntiles; t += 2) pair(t, std::true_type{});
+    // last product: V(ntiles-1) sits in V buffer (ntiles-1) % 2
+    if (ntiles & 1) {
+      begin(ntiles, lds, lds);
+      products(lds, lds + 2 * TILE_B, std::false_type{}, std::true_type{});
+    } else {
+      begin(ntiles, lds, lds);
+      products(lds, lds + 3 * TILE_B, std::false_type{}, std::true_type{});
+    }
   }
-  if (ntiles > 0) issue_loads(jb, lds);
-  int t = 0;
-  for (; t < t_lo; t += 2) pair(t, std::true_type{});
-  for (; t < t_hi; t += 2) pair(t, std::false_type{});
-  for (; t < ntiles; t += 2) pair(t, std::true_type{});
 
   // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
