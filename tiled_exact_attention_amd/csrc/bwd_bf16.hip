@@ -39,6 +39,32 @@
 namespace fattn {
 namespace {
 
+// LDS operand reads are issued this many matrix products ahead of their use.
+constexpr int kLA = 3;
+
+// sched_group_barrier sequences: N instructions of class M (0x008 matrix
+// product, 0x100 LDS read), or REP repetitions of (N1 of M1, N2 of M2).
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>), in order.
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+template <int M, int N>
+__device__ __forceinline__ void sched_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(M, N, 0);
+}
+template <int M1, int N1, int M2, int N2, int REP>
+__device__ __forceinline__ void sched_pairs() {
+  if constexpr (REP > 0) {
+    __builtin_amdgcn_sched_group_barrier(M1, N1, 0);
+    __builtin_amdgcn_sched_group_barrier(M2, N2, 0);
+    sched_pairs<M1, N1, M2, N2, REP - 1>();
+  }
+}
+
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per dQ block
@@ -473,21 +499,38 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   // half qh hold query row i0 + 32qh + 8(r/4) + 4hh + r%4 (the C layout of
   // S = Q K^T with one key per lane).
   auto compute = [&](int i0, const char* stage, auto masked) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(1);
+    // S = Q K^T and dP = dO V^T for both query halves: four interleaved
+    // accumulation chains, each operand read placed 2*kLA products ahead of
+    // its use (sched_group_barrier: 0x100 = LDS read, 0x008 = matrix product)
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      s[qh] = f32x16{};
-      dp[qh] = f32x16{};
+    {
+      bf16x8 qa[KSTEPS][2], da[KSTEPS][2];
 #pragma unroll
       for (int m = 0; m < KSTEPS; ++m) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + koff[m] + qh * 32 * ROWB);
-        s[qh] = mfma32(a, kf[m], s[qh]);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + qh * 32 * ROWB);
-        dp[qh] = mfma32(ad, vf[m], dp[qh]);
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          qa[m][qh] = *reinterpret_cast<const bf16x8*>(stage + koff[m] + qh * 32 * ROWB);
+          da[m][qh] = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + qh * 32 * ROWB);
+        }
       }
+#pragma unroll
+      for (int qh = 0; qh < 2; ++qh) {
+        s[qh] = f32x16{};
+        dp[qh] = f32x16{};
+      }
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m) {
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh) {
+          s[qh] = mfma32(qa[m][qh], kf[m], s[qh]);
+          dp[qh] = mfma32(da[m][qh], vf[m], dp[qh]);
+        }
+      }
+      sched_group<0x100, 2 * kLA>();
+      sched_pairs<0x008, 1, 0x100, 1, 4 * KSTEPS - 2 * kLA>();
+      sched_group<0x008, 2 * kLA>();
     }
-    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(masked)::value) {
       // pair (query qi, key) visible iff qi < Sq, key < Skv and the causal /
       // window rule holds; as bounds on qi: vis_lo <= qi < vis_hi
@@ -508,6 +551,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
+    // operand reads of the first kLA dV / dK products (product i: k-step
+    // i / (2 NB), output block (i / 2) % NB, dV if i is even, dK if odd)
+    constexpr int NPB = 8 * NB;
+    i16x4 ta[NPB][2];
+    auto read_t = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      constexpr int kc = i / (2 * NB), nb = (i / 2) % NB, src = (i & 1) ? 0 : TILE_B;
+      ta[i][0] = lds_read_tr16(stage + src + toff[nb][0] + kc * 16 * ROWB);
+      ta[i][1] = lds_read_tr16(stage + src + toff[nb][1] + kc * 16 * ROWB);
+    };
+    static_for<kLA>(read_t);
     // P = 2^(s c - lse2), dS = P (dP - D), both in the B layout of the
     // transposed products (k-step kc: registers 8(kc&1) .. +7 of half kc/2)
     const float* l2s = reinterpret_cast<const float*>(stage + 2 * TILE_B);
@@ -533,21 +587,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
       pf[kc] = to_bf16x8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
       dsf[kc] = to_bf16x8(sv[0], sv[1], sv[2], sv[3], sv[4], sv[5], sv[6], sv[7]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the dO / Q tiles)
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const i16x4 d0 = lds_read_tr16(stage + TILE_B + toff[nb][0] + kc * 16 * ROWB);
-        const i16x4 d1 = lds_read_tr16(stage + TILE_B + toff[nb][1] + kc * 16 * ROWB);
-        accv[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(d0, d1)), pf[kc], accv[nb]);
-        const i16x4 q0 = lds_read_tr16(stage + toff[nb][0] + kc * 16 * ROWB);
-        const i16x4 q1 = lds_read_tr16(stage + toff[nb][1] + kc * 16 * ROWB);
-        acck[nb] = mfma32(__builtin_bit_cast(bf16x8, concat_i16x4(q0, q1)), dsf[kc], acck[nb]);
+    // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the dO / Q
+    // tiles): eight accumulation chains; each step issues the reads of the
+    // product kLA ahead, then one product (sched_barrier fences keep the order)
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NPB>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i + kLA < NPB) read_t(std::integral_constant<int, i + kLA>{});
+      constexpr int kc = i / (2 * NB), nb = (i / 2) % NB;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, concat_i16x4(ta[i][0], ta[i][1]));
+      if constexpr ((i & 1) == 0) {
+        accv[nb] = mfma32(a, pf[kc], accv[nb]);
+      } else {
+        acck[nb] = mfma32(a, dsf[kc], acck[nb]);
       }
-    }
-    __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   // Whether this wave's keys see any / every query of tile [i0, i0 + 64).
