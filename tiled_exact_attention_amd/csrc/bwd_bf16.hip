@@ -39,8 +39,10 @@
 namespace fattn {
 namespace {
 
-// LDS operand reads are issued this many matrix products ahead of their use.
+// LDS operand reads are issued this many matrix products ahead of their use
+// (dK/dV kernel; the dQ kernel, at two waves per SIMD, has fewer registers).
 constexpr int kLA = 3;
+constexpr int kLAq = 2;
 
 // sched_group_barrier sequences: N instructions of class M (0x008 matrix
 // product, 0x100 LDS read), or REP repetitions of (N1 of M1, N2 of M2).
@@ -248,16 +250,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   // Order chosen for register pressure (two waves per SIMD): S^T, then P^T
   // packed to bf16 (the scores die), then dP^T, then dS^T.
   auto compute = [&](int64_t j0, const char* stage, auto masked) __attribute__((always_inline)) {
+    // S^T = K Q^T: the two 32-key chains interleaved, operand reads 2*kLAq
+    // products ahead (sched_group_barrier: 0x100 = LDS read, 0x008 = product)
     __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
+    {
+      bf16x8 ka[KSTEPS][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      for (int m = 0; m < KSTEPS; ++m)
 #pragma unroll
-      for (int m = 0; m < KSTEPS; ++m) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + koff[m] + kb * 32 * ROWB);
-        s[kb] = mfma32(a, qf[m], s[kb]);
-      }
+        for (int kb = 0; kb < 2; ++kb) ka[m][kb] = *reinterpret_cast<const bf16x8*>(stage + koff[m] + kb * 32 * ROWB);
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[m][kb], qf[m], s[kb]);
+      sched_group<0x100, 2 * kLAq>();
+      sched_pairs<0x008, 1, 0x100, 1, 2 * KSTEPS - 2 * kLAq>();
+      sched_group<0x008, 2 * kLAq>();
     }
     __builtin_amdgcn_s_setprio(0);
     if constexpr (decltype(masked)::value) {
@@ -282,17 +293,26 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
     // dP^T = V dO^T, then dS^T = P^T (dP^T - D)
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     f32x16 dp[2];
+    {
+      bf16x8 va[KSTEPS][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      dp[kb] = f32x16{};
+      for (int m = 0; m < KSTEPS; ++m)
 #pragma unroll
-      for (int m = 0; m < KSTEPS; ++m) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + kb * 32 * ROWB);
-        dp[kb] = mfma32(av, df[m], dp[kb]);
-      }
+        for (int kb = 0; kb < 2; ++kb) va[m][kb] = *reinterpret_cast<const bf16x8*>(stage + TILE_B + koff[m] + kb * 32 * ROWB);
+      dp[0] = f32x16{};
+      dp[1] = f32x16{};
+#pragma unroll
+      for (int m = 0; m < KSTEPS; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dp[kb] = mfma32(va[m][kb], df[m], dp[kb]);
+      sched_group<0x100, 2 * kLAq>();
+      sched_pairs<0x008, 1, 0x100, 1, 2 * KSTEPS - 2 * kLAq>();
+      sched_group<0x008, 2 * kLAq>();
     }
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
     bf16x8 dsf[4];
 #pragma unroll
