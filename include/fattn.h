@@ -205,8 +205,11 @@ FATTN_API int fattn_decode_int4(const void* q, const uint8_t* kq, const float* k
  * variable-length batch, [FA-3MOVES] CANN feature list): as
  * fattn_decode_int8 / fattn_decode_int4, with sequence b attending to its
  * first seqlens[b] cached tokens only.  Skv is the cache capacity (the
- * tensors' token dimension); the split plan and workspace size are those of
- * the capacity (fattn_decode_num_splits / _workspace_size with Skv).
+ * tensors' token dimension); the number of splits and the workspace size
+ * are those of the capacity (fattn_decode_num_splits / _workspace_size with
+ * Skv), and sequence b's tokens are cut into that many splits of
+ * ceil(seqlens[b] / splits) tokens rounded up to a multiple of 64 (splits
+ * past its end are empty).
  *
  * seqlens  [B] int32 device array, 0 <= seqlens[b] <= Skv; not checked on the
  *          host (values outside are clamped into [0, Skv]).  A sequence with

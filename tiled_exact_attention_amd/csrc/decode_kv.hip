@@ -168,11 +168,19 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   const float* ksb = p.ks + stream * p.Skv;
   const float* vsb = p.vs + stream * p.Skv;
 
-  // a sequence shorter than the cache leaves its later splits empty (o = 0,
-  // lse = -inf, weight 0 in the merge); lengths are clamped to [0, Skv]
-  const int len = p.seqlens ? min(max(p.seqlens[b], 0), p.Skv) : p.Skv;
-  const int t_begin = split * p.chunk;
-  const int t_end = min(len, t_begin + p.chunk);
+  // Variable lengths (clamped to [0, Skv]): each sequence's tokens are cut
+  // into nsplit splits of ceil(len / nsplit) tokens rounded up to whole
+  // tiles, so a batch shorter than the cache still uses every split slot
+  // (with the capacity's chunk a sequence of Skv/4 tokens would use a
+  // quarter of them).  Splits past the end are empty (o = 0, lse = -inf,
+  // weight 0 in the merge).
+  int len = p.Skv, chunk = p.chunk;
+  if (p.seqlens) {
+    len = min(max(p.seqlens[b], 0), p.Skv);
+    chunk = max(kDecodeTile, ((len + p.nsplit - 1) / p.nsplit + kDecodeTile - 1) / kDecodeTile * kDecodeTile);
+  }
+  const int t_begin = int(min(int64_t(split) * chunk, int64_t(len)));
+  const int t_end = min(len, t_begin + chunk);
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
   // query heads as the B operand.  k-step m covers, for lane group g,
