@@ -132,6 +132,9 @@ DECODE_VARLEN_CASES = [
     (3, 4, 4, 2050, 64, (64, 2050, 33), 8, 7),
     (4, 8, 2, 1000, 128, (999, 0, 2, 640), 4, 0),
     (2, 20, 1, 333, 64, (333, 100), 4, 3),
+    # many splits, per-sequence chunks that do not divide the lengths evenly
+    (2, 8, 2, 4096, 128, (1500, 4000), 8, 0),
+    (3, 4, 1, 3000, 64, (3000, 129, 2999), 4, 5),
 ]
 
 
