@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -241,6 +242,7 @@ def main():
     dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(args.steps)]
     pre_avg = sum(pre_ms) / len(pre_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
+    pre_med, dec_med = statistics.median(pre_ms), statistics.median(dec_ms)
     log(f"prefill avg {pre_avg * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us, wall {wall * 1e3 / args.steps:.3f} ms/step")
 
     result = {
@@ -272,11 +274,15 @@ def main():
                               "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                               "traffic": traffic, "kernel": "fwd_bf16_kernel<128>",
                               "algorithmic_flop_per_launch": flops,
-                              "avg_launch_us": round(pre_avg * 1e3, 2)}
+                              "avg_launch_us": round(pre_avg * 1e3, 2),
+                              "median_launch_us": round(pre_med * 1e3, 2),
+                              "min_launch_us": round(min(pre_ms) * 1e3, 2)}
     if do_decode:
         nbytes = decode_bytes(wd)
         gbs = nbytes / (dec_avg * 1e-3) / 1e9
         result["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "avg_call_us": round(dec_avg * 1e3, 2),
+                            "median_call_us": round(dec_med * 1e3, 2),
+                            "min_call_us": round(min(dec_ms) * 1e3, 2),
                             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                          "traffic": read_traffic(DECODE_KERNEL_SRC, "decode"),
@@ -284,6 +290,27 @@ def main():
                                          "algorithmic_bytes_per_call": nbytes}}
         if not do_prefill:
             result["value"], result["unit"] = round(gbs, 1), "GB/s"
+
+    if args.only == "all":
+        # side context: the device and the bandwidth a plain 1 GiB device copy reaches
+        props = torch.cuda.get_device_properties(dev)
+        csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cdst = torch.empty_like(csrc)
+        for _ in range(2):
+            cdst.copy_(csrc)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            cdst.copy_(csrc)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_us = c0.elapsed_time(c1) * 1e3 / 5
+        result["context"] = {"device": props.name, "compute_units": props.multi_processor_count,
+                             "copy_1GiB_GBps_read_plus_write": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
+                             "cache_note": "prefill inputs (192 MiB) fit the 256 MB last-level cache and are "
+                                           "not flushed between calls; the decode cache (2.2 GB) does not fit"}
+        del csrc, cdst
+        torch.cuda.empty_cache()
 
     if do_prefill and args.only == "all":
         # the other prefill workloads, informational (same kernel, same timing method)
