@@ -129,6 +129,9 @@ BF16_CASES = [
     (1, 4, 2, 150, 150, 64, True, 0, -0.2),       # negative scale
     (1, 2, 2, 90, 90, 128, True, 0, 0.0),         # zero scale: uniform rows
     (2, 8, 8, 64, 1000, 64, False, 0, None),      # non-causal, long keys
+    (1, 8, 2, 300, 900, 128, True, 200, None),    # window + continuation + GQA
+    (1, 4, 1, 513, 513, 64, True, 130, None),     # window over several tiles, G = 4
+    (2, 2, 2, 1030, 1030, 128, True, 257, None),  # long band: masked edges, unmasked pairs between
 ]
 
 
