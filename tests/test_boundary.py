@@ -136,6 +136,8 @@ def _fwd(**kw):
     (dict(d=96), FATTN_EUNSUPPORTED), (dict(d=256), FATTN_EUNSUPPORTED),
     (dict(dtype=2), FATTN_EUNSUPPORTED), (dict(dtype=-1), FATTN_EUNSUPPORTED),
     (dict(B=1 << 20, Hq=1 << 10, Hkv=1, Sq=1 << 12, Skv=4), FATTN_EINVAL),
+    # a 64-key tile of 2^18 kv heads x 128 no longer fits 32-bit offsets
+    (dict(Hq=1 << 18, Hkv=1 << 18, Sq=1, Skv=1, d=128), FATTN_EINVAL),
 ])
 def test_fwd_rejects_before_any_device_work(kw, want):
     assert _fwd(**kw) == want

@@ -163,6 +163,8 @@ int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   if (!fits(B, Sq, Hq, d) || !fits(B, Skv, Hkv, d)) return FATTN_EINVAL;
   // the kernels use one-dimensional grids of at most B*Hq*ceil(Sq/4) blocks
   if (int64_t(B) * Hq * ((int64_t(Sq) + 3) / 4) > 0x7fffffff) return FATTN_EINVAL;
+  // offsets inside a 64-key tile (64 rows of Hkv*d elements) are 32-bit
+  if (int64_t(Hkv) * d * 64 > 0x7fffffff) return FATTN_EINVAL;
   if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
   if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
 
@@ -190,6 +192,7 @@ int fattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float
   if (window < 0 || (window > 0 && !causal)) return FATTN_EINVAL;
   if (!fits(total_q, Hq, d, 1) || !fits(total_k, Hkv, d, 1)) return FATTN_EINVAL;
   if (int64_t(B) * Hq * ((int64_t(max_seqlen_q) + 3) / 4) > 0x7fffffff) return FATTN_EINVAL;
+  if (int64_t(Hkv) * d * 64 > 0x7fffffff) return FATTN_EINVAL;  // 32-bit offsets in a key tile
   if (dtype != FATTN_F32 && dtype != FATTN_BF16) return FATTN_EUNSUPPORTED;
   if (!supported_head_dim(d)) return FATTN_EUNSUPPORTED;
   if (total_q == 0) return FATTN_OK;  // no query rows: nothing to compute
