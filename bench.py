@@ -5,7 +5,9 @@ One step = one pass of the whole path over one batch of synthetic input:
     bf16), the workload the headline metric is quoted on, and
   * fattn_decode_int8 on the GQA int8-KV-cache decode workload (B=32, Hq=32,
     Hkv=8, Skv=32768, d=128).
-Inputs are resident in HBM before timing starts.  `value` is the prefill
+Inputs are resident in HBM before timing starts (two copies of the 2.2 GB
+decode cache, alternated from step to step, so no call finds the previous
+call's cache lines in the last-level cache).  `value` is the prefill
 attention throughput in TFLOP/s (4*d FLOPs per visible (query, key) pair per
 query head, counted exactly); the decode leg reports HBM GB/s over its
 algorithmic bytes (int8 K and V, their fp32 scales, the bf16 query and output).
@@ -26,6 +28,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -97,6 +100,39 @@ def read_traffic(kernel_src, key):
         return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def peak_clocks_mhz(device_index):
+    """Peak shader and memory clocks from hipDeviceGetAttribute, through the HIP
+    runtime this process already has loaded (attribute numbers from
+    hip_runtime_api.h: hipDeviceAttributeClockRate = 5, MemoryClockRate = 60,
+    both in kHz).  Empty if the runtime cannot be found."""
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        return {}
+    hip = ctypes.CDLL(path)
+    out = {}
+    for name, attr in (("peak_shader_clock_MHz", 5), ("peak_memory_clock_MHz", 60)):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), ctypes.c_int(attr), ctypes.c_int(device_index)) == 0:
+            out[name] = v.value / 1000
+    return out
+
+
 def time_cpu_baseline(w, q, k, v, budget_s):
     """Times the fp64 oracle on whole query rows of (b, h) pairs, growing the
     sample until about budget_s seconds of CPU work have been measured."""
@@ -127,6 +163,7 @@ def time_cpu_baseline(w, q, k, v, budget_s):
         "value": round(done_flops / elapsed / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{used} of {len(pairs)} (batch, head) pairs of the {w.name} workload, every "
                   f"query row, fp64 three-pass oracle; {done_flops / 1e9:.1f} GFLOP in {elapsed:.1f} s",
@@ -195,6 +232,10 @@ def main():
     if do_decode:
         log(f"generating {wd.name}")
         dq, dkq, dks, dvq, dvs = W.decode_workload_inputs(wd, device=dev)
+        # a second copy of the cache: timed calls alternate between the two, so
+        # no part of one call's cache can still sit in the last-level cache when
+        # the next call reads it
+        dcache = [(dkq, dks, dvq, dvs), tuple(t.clone() for t in (dkq, dks, dvq, dvs))]
         d_o = torch.empty_like(dq)
         d_lse = torch.empty((wd.B, wd.Hq), dtype=torch.float32, device=dev)
         ws = torch.empty((fa.decode_workspace_size(wd.B, wd.Hq, wd.Hkv, wd.Skv, wd.d, args.num_splits),),
@@ -208,20 +249,21 @@ def main():
         if st != 0:
             raise fa.FattnError(st, "fattn_fwd")
 
-    def run_decode():
-        st = fa.fattn_decode_int8(dq.data_ptr(), dkq.data_ptr(), dks.data_ptr(), dvq.data_ptr(),
-                                  dvs.data_ptr(), d_o.data_ptr(), d_lse.data_ptr(), wd.B, wd.Hq,
+    def run_decode(step):
+        ckq, cks, cvq, cvs = dcache[step % 2]
+        st = fa.fattn_decode_int8(dq.data_ptr(), ckq.data_ptr(), cks.data_ptr(), cvq.data_ptr(),
+                                  cvs.data_ptr(), d_o.data_ptr(), d_lse.data_ptr(), wd.B, wd.Hq,
                                   wd.Hkv, wd.Skv, wd.d, wd.scale, args.num_splits, ws.data_ptr(),
                                   ws.numel(), stream.cuda_stream)
         if st != 0:
             raise fa.FattnError(st, "fattn_decode_int8")
 
     log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    for s in range(args.warmup):
         if do_prefill:
             run_prefill()
         if do_decode:
-            run_decode()
+            run_decode(s)
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -234,7 +276,7 @@ def main():
             run_prefill()
         ev[s][1].record(stream)
         if do_decode:
-            run_decode()
+            run_decode(s)
         ev[s][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -305,10 +347,13 @@ def main():
         c1.record(stream)
         torch.cuda.synchronize()
         copy_us = c0.elapsed_time(c1) * 1e3 / 5
-        result["context"] = {"device": props.name, "compute_units": props.multi_processor_count,
+        result["context"] = {"device": props.name, "arch": props.gcnArchName,
+                             "compute_units": props.multi_processor_count,
+                             **peak_clocks_mhz(dev.index or 0),
                              "copy_1GiB_GBps_read_plus_write": round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1),
                              "cache_note": "prefill inputs (192 MiB) fit the 256 MB last-level cache and are "
-                                           "not flushed between calls; the decode cache (2.2 GB) does not fit"}
+                                           "not flushed between calls; the decode cache (2.2 GB) does not fit, "
+                                           "and the timed decode calls alternate between two copies of it"}
         del csrc, cdst
         torch.cuda.empty_cache()
 
@@ -337,7 +382,7 @@ def main():
     if args.only == "all":
         # next rows of the path, each timed the same way (informational)
         result["next"] = {}
-        del dq, dkq, dks, dvq, dvs
+        del dq, dkq, dks, dvq, dvs, dcache
         torch.cuda.empty_cache()
 
         def time_calls(fn, reps=10):
