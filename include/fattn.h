@@ -8,7 +8,11 @@
  * and holds no per-call state, so calls may be issued from several host
  * threads at once.  Work is enqueued asynchronously on `stream` (a
  * hipStream_t passed as void*; NULL is the null stream): buffers must stay
- * alive until that stream has finished the work.
+ * alive until that stream has finished the work.  A call makes no HIP call
+ * other than its kernel launches on `stream` (no allocation, memset, copy or
+ * synchronisation), so calls may be captured into a HIP graph; scalar
+ * arguments (sizes, scale, pos, num_splits) are then fixed at capture, while
+ * device data such as the varlen lengths is read at each replay.
  *
  * Every device pointer must be 16-byte aligned (allocator-returned pointers
  * are); a misaligned pointer is rejected with FATTN_EINVAL.
