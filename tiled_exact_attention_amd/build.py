@@ -28,11 +28,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; libfattn needs ROCm's hipcc to build")
 
 
+# Code-generation flags shared by the library build and the kernel-resource
+# check (the order is kept: hipcc derives its compilation-unit ids from it).
+ARCH_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17"]
+FEATURE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                 "-I", os.path.join(ROOT, "include")]
+DEVICE_FLAGS = ARCH_FLAGS + FEATURE_FLAGS
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-           "-Wall", "-Wno-unused-result", "-fvisibility=hidden",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    cmd = ([hipcc()] + ARCH_FLAGS + ["-fPIC", "-Wall", "-Wno-unused-result", "-fvisibility=hidden"]
+           + FEATURE_FLAGS + ["-c", src, "-o", obj])
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,6 +47,15 @@ def _compile(src: str, obj: str) -> None:
         raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{err}")
     if err.strip():
         sys.stderr.write(err + "\n")
+
+
+def device_assembly(src: str, out: str) -> None:
+    """Compile one HIP source's device code to gfx950 assembly (for the
+    register and occupancy report the compiler writes into it)."""
+    res = subprocess.run([hipcc()] + DEVICE_FLAGS + ["-S", "--cuda-device-only", src, "-o", out],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {os.path.basename(src)}:\n{res.stderr}")
 
 
 def build(verbose: bool = False) -> str:
