@@ -365,21 +365,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   for (; t < t_hi; t += 2) pair(t, std::false_type{});
   for (; t < ntiles; t += 2) pair(t, std::true_type{});
 
-  // ---- dQ = scale * (K^T dS^T)^T, bf16 (RNE)
-  if (!row_ok) return;
-  __bf16* qrow_out = p.dq + ((int64_t(b) * Sq + pos) * p.Hq + hq) * D;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 ov;
-      ov[0] = (__bf16)(acc[nb][4 * g + 0] * p.scale);
-      ov[1] = (__bf16)(acc[nb][4 * g + 1] * p.scale);
-      ov[2] = (__bf16)(acc[nb][4 * g + 2] * p.scale);
-      ov[3] = (__bf16)(acc[nb][4 * g + 3] * p.scale);
-      *reinterpret_cast<bf16x4*>(qrow_out + nb * 32 + 8 * g + 4 * hh) = ov;
-    }
-  }
+  // ---- dQ = scale * (K^T dS^T)^T, bf16 (RNE), written as whole rows through
+  // the stage the last step did not read (idle once that step's barrier has
+  // passed; each wave uses its own quarter)
+  store_tile_rows_bf16<D>(lds + (ntiles & 1) * STAGE_B + w * 32 * ROWB, acc, p.scale,
+                          [&](int r) -> __bf16* {
+                            const int prow = w * 32 + r;
+                            const int ppos = p0 + (prow >> p.gc_shift);
+                            return ppos < Sq ? p.dq + ((int64_t(b) * Sq + ppos) * p.Hq + hq0 +
+                                                       (prow & (gc - 1))) * D
+                                             : nullptr;
+                          });
 }
 
 // --------------------------------------------------------------------- dK, dV
@@ -662,9 +658,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   // ---- dK = scale * (Q^T dS)^T, dV = (dO^T P)^T: bf16 (RNE), or fp32
   // partials of this head split
-  if (!key_ok) return;
-  const int64_t ko = ((int64_t(b) * Skv + key) * p.Hkv + hk) * D;
   if (p.nsplit > 1) {
+    if (!key_ok) return;
+    const int64_t ko = ((int64_t(b) * Skv + key) * p.Hkv + hk) * D;
     const int64_t po = int64_t(split) * p.B * Skv * p.Hkv * D + ko;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -682,20 +678,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
     return;
   }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 kv4, vv4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kv4[e] = (__bf16)(acck[nb][4 * g + e] * p.scale);
-        vv4[e] = (__bf16)(accv[nb][4 * g + e]);
-      }
-      *reinterpret_cast<bf16x4*>(p.dk + ko + nb * 32 + 8 * g + 4 * hh) = kv4;
-      *reinterpret_cast<bf16x4*>(p.dv + ko + nb * 32 + 8 * g + 4 * hh) = vv4;
-    }
-  }
+  // whole key rows through the stage the last step did not read (idle once
+  // that step's barrier has passed; each wave uses its own quarter, first for
+  // dK, then for dV)
+  char* stage = lds + (niter & 1) * STAGE_B + w * 32 * ROWB;
+  store_tile_rows_bf16<D>(stage, acck, p.scale, [&](int r) -> __bf16* {
+    return jw + r < Skv ? p.dk + ((int64_t(b) * Skv + jw + r) * p.Hkv + hk) * D : nullptr;
+  });
+  store_tile_rows_bf16<D>(stage, accv, 1.f, [&](int r) -> __bf16* {
+    return jw + r < Skv ? p.dv + ((int64_t(b) * Skv + jw + r) * p.Hkv + hk) * D : nullptr;
+  });
 }
 
 // Sums the head-split partials of dK and dV in split order -> bf16; 8

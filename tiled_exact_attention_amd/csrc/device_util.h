@@ -121,6 +121,44 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
+// Writes one wave's 32 x D output tile as bf16 rows.  The tile is held in the
+// accumulator layout of the 32x32 matrix product (lane lq's values are row lq;
+// acc[nb][4g + e] is column nb*32 + 8g + 4*(lane/32) + e), each value times
+// mul.  The rows go through `stage` (this wave's own 32 * 2D bytes of LDS,
+// which no other wave may touch meanwhile) and leave as 16-byte stores of
+// whole rows: 4 rows per instruction at D = 128, 8 at D = 64, instead of
+// sixteen 8-byte pieces of 32 different rows per lane.  16-byte chunks are
+// XOR-swizzled by row so that neither the 8-byte writes (one chunk of 32 rows)
+// nor the 16-byte reads (whole rows) conflict in the LDS banks.  row_ptr(r)
+// gives the output address of tile row r, or nullptr to skip it.
+template <int D, class RowPtr>
+__device__ __forceinline__ void store_tile_rows_bf16(char* stage, const f32x16* acc, float mul,
+                                                     RowPtr row_ptr) {
+  constexpr int ROWB = 2 * D, KCH = D / 8, NB = D / 32, RPI = 1024 / ROWB;
+  static_assert(D == 64 || D == 128, "head dims of the kernels");
+  const int lane = threadIdx.x & 63, lq = lane & 31, hh = lane >> 5;
+  auto cswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+      v[0] = (__bf16)(acc[nb][4 * g + 0] * mul);
+      v[1] = (__bf16)(acc[nb][4 * g + 1] * mul);
+      v[2] = (__bf16)(acc[nb][4 * g + 2] * mul);
+      v[3] = (__bf16)(acc[nb][4 * g + 3] * mul);
+      *reinterpret_cast<bf16x4*>(stage + lq * ROWB + (((4 * nb + g) ^ cswz(lq)) << 4) + 8 * hh) = v;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / KCH, c = lane % KCH;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + r * ROWB + ((c ^ cswz(r)) << 4));
+    __bf16* dst = row_ptr(r);
+    if (dst) *reinterpret_cast<uint4*>(dst + c * 8) = v;
+  }
+}
+
 // Rows and lengths of one sequence: dense batches index b * S; packed batches
 // read the cumulative offsets, clamped so that no value can address memory
 // outside the packed tensors (Sq of a packed batch is the longest query

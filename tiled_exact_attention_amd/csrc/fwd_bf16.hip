@@ -408,41 +408,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log).
   // Each wave stages its 32 output rows in its own quarter of the two K
   // buffers, which no wave reads and no copy targets after the barrier that
-  // opened the last iteration, then writes whole rows with 16-byte stores:
-  // 4 (d = 128) or 8 (d = 64) contiguous rows per instruction instead of 16
-  // eight-byte pieces of 32 rows.  Measured on MI355X: 2-5% off the launch
-  // (the epilogue of a 128-row block went from about 2.7 to 1.8 us).
+  // opened the last iteration, and writes whole rows with 16-byte stores.
+  // Measured on MI355X: 2-5% off the launch (the epilogue of a 128-row block
+  // went from about 2.7 to 1.8 us).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  {
-    // row-major rows, 16-byte chunks XOR-swizzled by row so that neither the
-    // 8-byte writes (one chunk of 32 rows) nor the 16-byte reads (whole rows)
-    // conflict in the LDS banks
-    char* stage = lds + w * 32 * ROWB;
-    auto oswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
-        ov[0] = (__bf16)(acc[nb][4 * g + 0] * inv);
-        ov[1] = (__bf16)(acc[nb][4 * g + 1] * inv);
-        ov[2] = (__bf16)(acc[nb][4 * g + 2] * inv);
-        ov[3] = (__bf16)(acc[nb][4 * g + 3] * inv);
-        *reinterpret_cast<bf16x4*>(stage + lq * ROWB + (((4 * nb + g) ^ oswz(lq)) << 4) + 8 * hh) = ov;
-      }
-    }
-    constexpr int RPI = 1024 / ROWB;  // rows per 1 KB store
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = i * RPI + lane / KCH, c = lane % KCH;
-      const uint4 val = *reinterpret_cast<const uint4*>(stage + r * ROWB + ((c ^ oswz(r)) << 4));
-      const int prow = w * 32 + r;
-      const int ppos = p0 + (prow >> p.gc_shift);
-      if (ppos < Sq)
-        *reinterpret_cast<uint4*>(p.o + ((sv.q_row0 + ppos) * p.Hq + hq0 + (prow & (gc - 1))) * D + c * 8) = val;
-    }
-  }
+  store_tile_rows_bf16<D>(lds + w * 32 * ROWB, acc, inv, [&](int r) -> __bf16* {
+    const int prow = w * 32 + r;
+    const int ppos = p0 + (prow >> p.gc_shift);
+    return ppos < Sq ? p.o + ((sv.q_row0 + ppos) * p.Hq + hq0 + (prow & (gc - 1))) * D : nullptr;
+  });
   if (!row_ok) return;
   if (hh == 0 && p.lse) {
     p.lse[sv.lse0 + int64_t(hq) * sv.lse_hs + pos] =
