@@ -165,7 +165,8 @@ FATTN_API size_t fattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
  * The keys are cut into splits processed in parallel, each producing a
  * partial (o_s, lse_s) in the workspace; a second kernel merges them by
  * log-sum-exp (the local-max-and-sum correction of the [FA-NPU] tiling
- * section applied across splits).
+ * section applied across splits).  With a single split the output is
+ * written directly and the merge kernel is not launched.
  *
  * q          [B, Hq, d] bf16          (the [B, 1, Hq, d] query of the new token)
  * kq, vq     [B, Hkv, Skv, d] int8    (head-major cache: one contiguous stream

@@ -9,7 +9,9 @@
 // (batch, kv head) stream are cut into splits; each split runs the online
 // softmax of the [FA-NPU] tiling section over its tokens and writes a
 // normalised partial output and its log-sum-exp; a second kernel merges the
-// partials (global max of the partial lse, weights e^(lse_s - max)).
+// partials (global max of the partial lse, weights e^(lse_s - max)).  With a
+// single split the split kernel writes the output and lse itself and the
+// merge is not launched (its result would be the same bits).
 //
 // gfx950 design (split kernel): one wave per (batch, kv head, chunk of <= 16
 // query heads, split).  Per 32-token tile:
@@ -68,6 +70,8 @@ struct SplitParams {
   const float* vs;
   float* part_o;
   float* part_lse;
+  __bf16* o;    // final output [B, Hq, d] when nsplit == 1 (no merge)
+  float* lse;   // final lse [B, Hq] or null, when nsplit == 1
   const int* seqlens;  // [B] tokens each sequence sees (first seqlens[b]), or null: all Skv
   int Hq, Hkv, Skv;
   int G;        // query heads per kv head
@@ -371,6 +375,30 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   l_tot += __shfl_xor(l_tot, 32);
   if (!head_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_row = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+  if (p.nsplit == 1) {
+    // a single split is the whole row: write the bf16 output and lse here
+    // (what the merge would produce: weight exp(0) = 1, log 1 = 0)
+    __bf16* orow = p.o + (int64_t(b) * p.Hq + hq) * D;
+    if constexpr (BITS == 8) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const f32x4 v = acc[cb] * inv;
+        bf16x4 h;
+        h[0] = (__bf16)v[0]; h[1] = (__bf16)v[1]; h[2] = (__bf16)v[2]; h[3] = (__bf16)v[3];
+        *reinterpret_cast<bf16x4*>(orow + 16 * cb + 4 * g) = h;
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < GM::NREAD; ++cb) {
+        const f32x4 e = (acc[2 * cb] - pbias) * inv, o = (acc[2 * cb + 1] - pbias) * inv;
+        *reinterpret_cast<bf16x8*>(orow + 32 * cb + 8 * g) =
+            to_bf16x8(e[0], o[0], e[1], o[1], e[2], o[2], e[3], o[3]);
+      }
+    }
+    if (g == 0 && p.lse) p.lse[int64_t(b) * p.Hq + hq] = lse_row;
+    return;
+  }
   const int64_t prow = (int64_t(b) * p.Hq + hq) * p.nsplit + split;
   float* po = p.part_o + prow * D;
   if constexpr (BITS == 8) {
@@ -389,7 +417,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
       *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
     }
   }
-  if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+  if (g == 0) p.part_lse[prow] = lse_row;
 }
 
 // One wave per (batch, query head): merges nsplit partials by log-sum-exp.
@@ -429,8 +457,9 @@ template <int D, int BITS>
 void launch_split_and_merge(const DecodeArgs& a, const SplitParams& p, unsigned waves,
                             unsigned rows, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<D, BITS>), dim3(waves), dim3(64), 0, stream, p);
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(rows), dim3(64), 0, stream,
-                     a.part_o, a.part_lse, static_cast<__bf16*>(a.o), a.lse, a.nsplit);
+  if (a.nsplit > 1)  // one split writes the output itself
+    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(rows), dim3(64), 0, stream,
+                       a.part_o, a.part_lse, static_cast<__bf16*>(a.o), a.lse, a.nsplit);
 }
 
 }  // namespace
@@ -444,6 +473,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.vs = a.vscale;
   p.part_o = a.part_o;
   p.part_lse = a.part_lse;
+  p.o = static_cast<__bf16*>(a.o);
+  p.lse = a.lse;
   p.seqlens = a.seqlens;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
