@@ -53,10 +53,14 @@ constexpr int kBN = 64;           // keys per tile
 constexpr float kNegHuge = -1e30f;
 constexpr float kLn2 = 0.693147180559945309f;
 // The accumulator and row sum are kept relative to a reference max m_ref
-// (base-2 units) that is only raised when a row's running max exceeds it by
-// more than kLazy; probabilities are then at most 2^kLazy.  Numerator and
-// denominator share m_ref, so the result is the same softmax.
+// (base-2 units), set to the row max on a wave's first tile and afterwards
+// raised only when some probability of a tile would exceed 2^kLazy.  A lane's
+// partial sum of the tile's probabilities exceeds 2^kLazy whenever one of
+// them does, so the steady state tests that sum and takes no max over the
+// scores; only then is the tile's max taken and its probabilities recomputed.
+// Numerator and denominator share m_ref, so the result is the same softmax.
 constexpr float kLazy = 8.f;
+constexpr float kSumLimit = 256.f;  // 2^kLazy
 // LDS operand reads are issued this many matrix products ahead of their use.
 constexpr int kLA = 3;
 
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
 
   // ---- S(t) -> P(t): mask (only on tiles that straddle an edge of this
   // wave's band), online softmax in base 2 with the scale folded into c.
-  auto softmax = [&](int64_t j0, auto masked) __attribute__((always_inline)) {
+  auto softmax = [&](int64_t j0, auto masked, auto first) __attribute__((always_inline)) {
     // key j0 + kofs is visible iff row_lo <= key < row_hi; kofs - 4*hh is a
     // compile-time constant per register, so compare against shifted bounds.
     if constexpr (decltype(masked)::value) {
@@ -318,30 +322,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         }
       }
     }
-    float mx = kNegHuge;
+    auto raise_reference = [&]() __attribute__((always_inline)) {
+      float mx = kNegHuge;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    }
-    mx = max_across_halves(mx) * p.c;
-    if (__builtin_expect(__any(mx > m_run + kLazy), 0)) {  // rare: raise the reference
-      const float m_new = fmaxf(m_run, mx);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      }
+      mx = max_across_halves(mx) * p.c;
+      return mx;
+    };
+    auto rescale_to = [&](float m_new) __attribute__((always_inline)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[nb] *= alpha;
-    }
+    };
+    auto exponentials = [&]() __attribute__((always_inline)) {
+      float ps = 0.f;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      float e[8];
+      for (int kc = 0; kc < 4; ++kc) {
+        float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -m_run));
-        l_run += e[i];
+        for (int i = 0; i < 8; ++i) {
+          e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -m_run));
+          ps += e[i];
+        }
+        pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       }
-      pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      return ps;
+    };
+    if constexpr (decltype(first)::value) {
+      // first tile: the reference is the row max
+      const float mx = raise_reference();
+      if (__any(mx > m_run + kLazy)) rescale_to(fmaxf(m_run, mx));
+      l_run += exponentials();
+    } else {
+      // later tiles keep the reference unless some exponential exceeds 2^kLazy,
+      // which the lane's partial sum reveals without a max over the scores
+      float ps = exponentials();
+      if (__builtin_expect(__any(ps > kSumLimit), 0)) {  // rare: raise the reference
+        const float mx = raise_reference();
+        rescale_to(fmaxf(m_run, mx));
+        ps = exponentials();
+      }
+      l_run += ps;
     }
   };
 
@@ -369,7 +395,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     constexpr int cur = decltype(odd)::value ? 1 : 0;
     const int64_t j0 = begin(t, lds + (cur ^ 1) * TILE_B, lds + (2 + cur) * TILE_B);
     products(lds + cur * TILE_B, lds + (2 + (cur ^ 1)) * TILE_B, std::true_type{}, std::true_type{});
-    softmax(j0, masked);
+    softmax(j0, masked, std::false_type{});
   };
   auto pair = [&](int t, auto masked) __attribute__((always_inline)) {
     iteration(t, std::true_type{}, masked);
@@ -389,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     {
       const int64_t j0 = begin(0, lds + TILE_B, lds + 2 * TILE_B);
       products(lds, lds, std::true_type{}, std::false_type{});
-      softmax(j0, std::true_type{});
+      softmax(j0, std::true_type{}, std::true_type{});
     }
     int t = 1;
     for (; t < t_lo && t < ntiles; t += 2) pair(t, std::true_type{});
