@@ -123,6 +123,34 @@ def prefill_inputs(B, Hq, Hkv, Sq, Skv, d, dtype="bf16", seed=0, device="cpu"):
     return _cast(q, dtype), _cast(k, dtype), _cast(v, dtype)
 
 
+def key_drift(Skv, profile, step):
+    """Per-key amplitudes a_j [Skv] (fp32, CPU): "rise" a_j = step * j, "fall"
+    step * (Skv - 1 - j), "spikes" n * step at key 150 n - 50 (n = 1, 2, ...: keys
+    100, 250, 400, ...) and 0 elsewhere."""
+    j = torch.arange(Skv, dtype=torch.float32)
+    if profile == "rise":
+        return step * j
+    if profile == "fall":
+        return step * (Skv - 1 - j)
+    if profile == "spikes":
+        return torch.where(j % 150 == 100, step * (torch.div(j, 150, rounding_mode="floor") + 1), torch.tensor(0.0))
+    raise ValueError(profile)
+
+
+def drifting_inputs(B, Hq, Hkv, Sq, Skv, d, profile, step, dtype="bf16", seed=0, device="cpu"):
+    """prefill_inputs' draws with every Q row moved by 2 and key j by a_j (key_drift)
+    along the all-ones direction, before the cast: a score then carries an extra
+    2 * a_j * d * scale, so along the keys the scores climb, fall, or jump at
+    isolated keys far above every earlier one."""
+    g = _gen(seed, device)
+    q = torch.randn((B, Sq, Hq, d), generator=g, device=device, dtype=torch.float32)
+    k = torch.randn((B, Skv, Hkv, d), generator=g, device=device, dtype=torch.float32)
+    v = torch.randn((B, Skv, Hkv, d), generator=g, device=device, dtype=torch.float32)
+    q += 2.0
+    k += key_drift(Skv, profile, step).to(device).view(1, Skv, 1, 1)
+    return _cast(q, dtype), _cast(k, dtype), _cast(v, dtype)
+
+
 def workload_inputs(w: Prefill, device="cpu"):
     return prefill_inputs(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.d, w.dtype, w.seed, device)
 
@@ -180,19 +208,25 @@ def quantize_rows_int4(x: torch.Tensor):
     return packed.to(torch.uint8), scale.to(torch.float32)
 
 
-def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False, bits=8):
+def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False, bits=8, k_drift=None):
     """q [B,Hq,d] bf16; kq/vq [B,Hkv,Skv,d] int8 (bits=8) or [B,Hkv,Skv,d/2]
     uint8 holding two int4 codes per byte (bits=4); k_scale/v_scale [B,Hkv,Skv] fp32.
 
     Draw order: Q, then for each batch entry K_b [Hkv,Skv,d] and V_b, each
     quantised as soon as it is drawn (so host memory stays at one slice).
     With keep_float=True the unquantised fp32 K and V are returned as well.
+    With k_drift (a [Skv] tensor from key_drift) Q is moved by 2 and key j by
+    k_drift[j] along the all-ones direction before quantisation.
     """
     if bits not in (8, 4):
         raise ValueError(bits)
     quantize_rows = quantize_rows_int8 if bits == 8 else quantize_rows_int4
     g = _gen(seed, device)
-    q = torch.randn((B, Hq, d), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device=device, dtype=torch.float32)
+    if k_drift is not None:
+        q += 2.0
+        k_drift = k_drift.to(device=device, dtype=torch.float32).view(1, Skv, 1)
+    q = q.to(torch.bfloat16)
     if bits == 8:
         kq = torch.empty((B, Hkv, Skv, d), dtype=torch.int8, device=device)
     else:
@@ -206,6 +240,8 @@ def decode_inputs(B, Hq, Hkv, Skv, d, seed=0, device="cpu", keep_float=False, bi
         vf = torch.empty_like(kf)
     for b in range(B):
         kb = torch.randn((Hkv, Skv, d), generator=g, device=device, dtype=torch.float32)
+        if k_drift is not None:
+            kb += k_drift
         kq[b], ks[b] = quantize_rows(kb)
         if keep_float:
             kf[b] = kb
