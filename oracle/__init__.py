@@ -64,7 +64,7 @@ def _load(path: str | None = None):
         lib.oracle_fwd_varlen_rows.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                f64, i32, i32, vp, i64, vp, vp, i32]
         lib.oracle_fwd_varlen_rows.restype = i32
-        lib.oracle_bwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, i32, i32,
+        lib.oracle_bwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f64, i32, i32,
                                    vp, vp, vp, i32]
         lib.oracle_bwd.restype = i32
         lib.oracle_max_threads.argtypes = [i32]
@@ -136,13 +136,18 @@ def fwd(q, k, v, *, causal: bool, window: int = 0, scale: float | None = None,
 
 
 def bwd(q, k, v, dout, *, causal: bool, window: int = 0, scale: float | None = None,
-        threads: int = 0, lib: str | None = None):
+        o=None, threads: int = 0, lib: str | None = None):
     """Gradients (dq, dk, dv) of exact attention for an upstream gradient dout, in fp64.
 
     q, dout: [B, Sq, Hq, d]; k, v: [B, Skv, Hkv, d].  dk and dv of a kv head sum
     over the query heads sharing it.  Returns arrays shaped like q, k, v.
+    o (optional, like q): a stored forward output; the row term D is then formed
+    as dout . o (equal to the default for the exact output, see oracle.c).
     """
     qd, kd, vd, dod = _f64(q), _f64(k), _f64(v), _f64(dout)
+    od = None if o is None else _f64(o)
+    if od is not None and od.shape != qd.shape:
+        raise ValueError("o must be shaped like q")
     B, Sq, Hq, d = qd.shape
     Bk, Skv, Hkv, dk_ = kd.shape
     if (Bk, dk_) != (B, d) or vd.shape != kd.shape or dod.shape != qd.shape:
@@ -152,7 +157,8 @@ def bwd(q, k, v, dout, *, causal: bool, window: int = 0, scale: float | None = N
     dq = np.empty_like(qd)
     dk = np.empty_like(kd)
     dv = np.empty_like(vd)
-    rc = _load(lib).oracle_bwd(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod), B, Hq, Hkv, Sq, Skv, d,
+    rc = _load(lib).oracle_bwd(_ptr(qd), _ptr(kd), _ptr(vd), _ptr(dod), None if od is None else _ptr(od),
+                               B, Hq, Hkv, Sq, Skv, d,
                                float(scale), int(bool(causal)), int(window),
                                _ptr(dq), _ptr(dk), _ptr(dv), int(threads))
     if rc != 0:

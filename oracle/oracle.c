@@ -437,6 +437,11 @@ int oracle_kv_quantize_int4(const float* x, uint8_t* codes, float* scales,
  * contributes nothing and gets dQ_i = 0.  dK and dV of a kv head sum over the
  * query heads sharing it.  Layouts as oracle_fwd_rows; dO, dq like q; dk, dv
  * like k (all double).
+ * o (may be NULL; laid out like q): a stored forward output.  When given,
+ * D_i is formed from it as dO_i . O_i, the same quantity by the identity
+ * sum_j P_ij (dO_i . V_j) = dO_i . (sum_j P_ij V_j) = dO_i . O_i; a backward
+ * that starts from the saved output ([FA-NPU] recomputation section) sees
+ * that output as it was stored, rounding included.
  * Pass 1 (one thread per query row): the row's P by the forward's three
  * passes, its dP, D_i and dQ_i; it keeps lse_i = m + log(l) and D_i.
  * Pass 2 (one thread per key of a kv head): P_ij = exp(scale q_i.k_j - lse_i),
@@ -444,7 +449,7 @@ int oracle_kv_quantize_int4(const float* x, uint8_t* codes, float* scales,
  * Neither pass depends on the thread count.
  */
 int oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
-               int B, int Hq, int Hkv, int Sq, int Skv, int d,
+               const double* o, int B, int Hq, int Hkv, int Sq, int Skv, int d,
                double scale, int causal, int window,
                double* dq, double* dk, double* dv, int nthreads) {
   if (bad_shape(B, Hq, Hkv, Sq, Skv, d) || window < 0 || (window > 0 && !causal)) return ORACLE_BAD_ARGS;
@@ -512,6 +517,12 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
         for (c = 0; c < d; c++) acc += doi[c] * vh[j * kv_stride + c];
         dp[j - jlo] = acc;
         D += p[j - jlo] * acc;
+      }
+      if (o) {
+        const double* oi = o + ((b * Sq + i) * Hq + h) * (int64_t)d;
+        double Do = 0.0;
+        for (c = 0; c < d; c++) Do += doi[c] * oi[c];
+        D = Do;
       }
       for (j = jlo; j < jhi; j++) {
         double dsq = p[j - jlo] * (dp[j - jlo] - D);

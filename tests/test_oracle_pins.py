@@ -653,6 +653,32 @@ def pin_bwd_sum_invariants(lib):
         assert np.allclose(dv.sum(axis=1), want, atol=1e-12)
 
 
+def pin_bwd_stored_output(lib):
+    # D formed from a stored output: with the exact output it must give the
+    # default result (D_i = sum_j P_ij dP_ij = dO_i . O_i); moving one stored
+    # element O_ic by delta moves D_i by delta dO_ic, hence dQ_i by
+    # -scale delta dO_ic sum_j P_ij K_j (the forward with V := K gives that sum)
+    # and leaves other rows' dQ and every dV unchanged.  GQA, Sq > Skv, window.
+    B, Sq, Skv, Hq, Hkv, d = 2, 7, 5, 4, 2, 6
+    q, k, v = _rand((B, Sq, Hq, d), 79), _rand((B, Skv, Hkv, d), 80), _rand((B, Skv, Hkv, d), 81)
+    do = _rand((B, Sq, Hq, d), 82)
+    for causal, window in ((False, 0), (True, 0), (True, 2)):
+        o, _ = oracle.fwd(q, k, v, causal=causal, window=window, scale=0.7)
+        ref = oracle.bwd(q, k, v, do, causal=causal, window=window, scale=0.7, lib=lib)
+        got = oracle.bwd(q, k, v, do, causal=causal, window=window, scale=0.7, o=o, lib=lib)
+        for a, r in zip(got, ref):
+            assert np.allclose(a, r, atol=1e-12, rtol=0), (causal, window)
+        b, i, h, c, delta = 1, Sq - 1, 3, 2, 0.25
+        o2 = o.copy()
+        o2[b, i, h, c] += delta
+        dq2, _, dv2 = oracle.bwd(q, k, v, do, causal=causal, window=window, scale=0.7, o=o2, lib=lib)
+        pk, _ = oracle.fwd(q, k, k, causal=causal, window=window, scale=0.7)
+        want = got[0].copy()
+        want[b, i, h] -= 0.7 * delta * do[b, i, h, c] * pk[b, i, h]
+        assert np.allclose(dq2, want, atol=1e-12, rtol=0), (causal, window)
+        assert np.allclose(dv2, got[2], atol=1e-12, rtol=0)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -705,6 +731,9 @@ MUTANTS = {
     "bwd weights without lse": ("double pij = exp(scale * s - row_lse[r]);", "double pij = exp(scale * s);"),
     "bwd dk from k": ("dkj[c] += scale * dsk * qi[c];", "dkj[c] += scale * dsk * kj[c];"),
     "bwd dv from q": ("dvj[c] += pij * doi[c];", "dvj[c] += pij * qi[c];"),
+    "bwd stored output without dout": ("for (c = 0; c < d; c++) Do += doi[c] * oi[c];", "for (c = 0; c < d; c++) Do += oi[c];"),
+    "bwd stored output of head 0": ("const double* oi = o + ((b * Sq + i) * Hq + h) * (int64_t)d;",
+                                    "const double* oi = o + ((b * Sq + i) * Hq) * (int64_t)d;"),
     "quantiser rounds half away from zero": ("float r = rintf(qv);", "float r = roundf(qv);"),
     "quantiser ignores the append position": ("int64_t slot = (b * Hkv + h) * (int64_t)cap + pos + t;",
                                              "int64_t slot = (b * Hkv + h) * (int64_t)cap + t;"),

@@ -14,10 +14,11 @@ K are shifted along one direction (workloads.drifting_inputs) so that
 * "fall":   the first tile holds the largest scores and later tiles underflow
             towards 0 (the reference is never raised).
 
-Each case first checks on the host that its scores really climb past the lazy
-bound between tiles (for rise and spikes), then compares prefill and decode with
-the fp64 oracle at the usual bounds: bf16 max-abs 2e-2, mean-abs 2e-3, lse
-max-abs 1e-3.
+Each prefill case first checks on the host that its scores really climb past
+the lazy bound between tiles (for rise and spikes); prefill and decode are
+compared with the fp64 oracle at the usual bounds (bf16 max-abs 2e-2, mean-abs
+2e-3, lse max-abs 1e-3), the backward at the usual gradient bounds with D formed
+from the stored bf16 output (see its test).
 """
 from __future__ import annotations
 
@@ -141,3 +142,49 @@ def test_decode_with_climbing_scores(case, cuda_device):
     _say(f"  max-abs {err.max():.3e} mean-abs {err.mean():.3e} lse {le:.3e} (lse up to {np.abs(lse_ref).max():.1f})")
     assert np.all(np.isfinite(o))
     assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN and le <= BF16_LSE
+
+
+GRAD_MAX_REL, GRAD_MEAN_REL, GRAD_MAX_ABS, GRAD_MEAN_ABS = 2.0 ** -6, 2.0 ** -7, 1e-4, 1e-5
+BWD = [
+    (1, 4, 2, 600, 600, 128, True, 0, "rise"),
+    (1, 8, 1, 500, 500, 64, True, 0, "spikes"),
+    (1, 4, 4, 300, 700, 128, False, 0, "spikes"),
+]
+
+
+@pytest.mark.parametrize("case", BWD, ids=[str(c) for c in BWD])
+def test_bwd_with_climbing_scores(case, cuda_device):
+    # The backward recomputes P = exp(s - lse) with lse far from 0, and forms
+    # D_i = dO_i . O_i from the stored bf16 output.  With P nearly one-hot,
+    # dS = P (dP - D) is a small difference, so the rounding of the stored O
+    # (2^-9 relative) sets the error of dQ and dK rather than the products'.
+    # The oracle therefore forms D from its own forward output rounded to bf16
+    # (RNE), as stored; bounds as for every gradient (2^-6 of the max, 2^-7 of
+    # the rms, relative to each gradient's own scale).
+    B, Hq, Hkv, Sq, Skv, d, causal, window, profile = case
+    _say(f"case rescale bwd {case}")
+    scale = 1 / math.sqrt(d)
+    seed = Sq + d + 7
+    q, k, v = W.drifting_inputs(B, Hq, Hkv, Sq, Skv, d, profile, _step(profile, d), "bf16", seed=seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    do = torch.randn(B, Sq, Hq, d, generator=g).to(torch.bfloat16)
+    dev = cuda_device
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, window=window, scale=scale, return_lse=True)
+    poison = lambda t: torch.full_like(t, float("nan"))
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, lse, dod, causal=causal, window=window, scale=scale,
+                        out=(poison(qd), poison(kd), poison(vd)))
+    torch.cuda.synchronize()
+    o_ref, _ = oracle.fwd(q, k, v, causal=causal, window=window, scale=scale)
+    o_stored = torch.from_numpy(o_ref).to(torch.bfloat16)
+    refs = oracle.bwd(q, k, v, do, causal=causal, window=window, scale=scale, o=o_stored)
+    msg = []
+    for name, a, r in (("dq", dq, refs[0]), ("dk", dk, refs[1]), ("dv", dv, refs[2])):
+        a = _np64(a)
+        assert np.all(np.isfinite(a)), f"{name}: non-finite gradient"
+        err = np.abs(a - r)
+        mx, rms = np.abs(r).max(), math.sqrt(float((r ** 2).mean()))
+        msg.append(f"{name} {err.max() / max(mx, 1e-30):.2e}/{err.mean() / max(rms, 1e-30):.2e}")
+        assert err.max() <= GRAD_MAX_REL * mx + GRAD_MAX_ABS, f"{name}: max {err.max():.3e} (ref {mx:.3e})"
+        assert err.mean() <= GRAD_MEAN_REL * rms + GRAD_MEAN_ABS, f"{name}: mean {err.mean():.3e} (rms {rms:.3e})"
+    _say("  rel max/mean: " + " ".join(msg))
