@@ -71,8 +71,10 @@ typedef enum {
  * the definition in [FA-NPU] (section on why attention is so memory-hungry)
  * computed tile by tile with an online softmax ([FA-NPU] tiling section;
  * [FA-3MOVES] moves 1 and 2): each query tile streams key/value tiles, keeps
- * a running row max and row sum, rescales its accumulator, and never writes
- * the Sq x Skv score matrix to memory.
+ * per row a running maximum used as the exponent reference and a running sum,
+ * rescales its accumulator when the reference rises, and never writes the
+ * Sq x Skv score matrix to memory.  The reference is raised lazily (only when
+ * a tile's probabilities would exceed 2^8), which leaves the softmax unchanged.
  *
  * q    [B, Sq, Hq, d]   (batch, sequence, heads, head_dim: the order of the
  *                        usage section of [FA-NPU])
