@@ -25,7 +25,7 @@ _libs: dict = {}
 
 def compile_source(src: str, out: str) -> str:
     """Compile a C source of the oracle into a shared library with gcc."""
-    tmp = out + ".tmp"
+    tmp = f"{out}.tmp{os.getpid()}"  # one per process: concurrent builders do not collide
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
            "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True)
@@ -33,16 +33,21 @@ def compile_source(src: str, out: str) -> str:
     return out
 
 
+def _stale() -> bool:
+    """liboracle.so missing or older than oracle.c (its signatures may differ)."""
+    return not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(SOURCE)
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so (no fast-math, no intrinsics)."""
-    if force or not os.path.exists(_LIB):
+    if force or _stale():
         compile_source(SOURCE, _LIB)
     return _LIB
 
 
 def _load(path: str | None = None):
     if path is None:
-        if not os.path.exists(_LIB):
+        if _stale():
             build(force=False)
         path = _LIB
     if path not in _libs:
