@@ -175,10 +175,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "copy"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "copy", "bwd"), default="all",
                     help="time one leg only (for profiler runs); the JSON line is then partial. "
                          "'copy' times a plain 1 GiB device-to-device copy, the known-size "
-                         "reference that scales the HBM byte counters")
+                         "reference that scales the HBM byte counters; 'bwd' times the backward "
+                         "of the prefill workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--num-splits", type=int, default=0, help="decode key splits (0 = library default)")
@@ -220,6 +221,30 @@ def main():
         return
 
     wp, wd = W.MHA_CAUSAL, W.INT8_DECODE
+    if args.only == "bwd":
+        # the backward alone (forward once for o and lse, then K timed calls)
+        q, k, v = (t.to(dev) for t in W.workload_inputs(wp))
+        bdo = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(wp.seed + 100),
+                          device=dev).to(torch.bfloat16)
+        o, lse = fa.fwd(q, k, v, causal=wp.causal, scale=wp.scale, return_lse=True)
+        bws = torch.empty((fa.fattn_bwd_workspace_size(wp.B, wp.Hq, wp.Hkv, wp.Sq, wp.Skv, wp.d),),
+                          dtype=torch.uint8, device=dev)
+        bout = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        call = lambda: fa.bwd(q, k, v, o, lse, bdo, causal=wp.causal, scale=wp.scale, workspace=bws, out=bout)
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / max(args.steps, 1)
+        bflops = 2.5 * prefill_flops(wp)
+        print(json.dumps({"workload": f"backward of {wp.name}", "avg_us": round(us, 2),
+                          "TFLOP/s": round(bflops / (us * 1e-6) / 1e12, 2)}), flush=True)
+        return
     do_prefill = args.only in ("all", "prefill")
     do_decode = args.only in ("all", "decode")
 
