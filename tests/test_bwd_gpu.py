@@ -109,22 +109,3 @@ def test_bwd_is_bitwise_repeatable(cuda_device):
     b = fa.bwd(q, k, v, o, lse, do, causal=True)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
-
-
-@pytest.mark.parametrize("w", [W.MHA_CAUSAL, W.GQA_CAUSAL], ids=lambda w: w.name)
-def test_full_size_bwd_sampled_groups(w, cuda_device):
-    # the full workload on the GPU; two whole (batch, kv head) groups against the oracle
-    _say(f"case bwd full size: {w.name}")
-    q, k, v = W.workload_inputs(w)
-    g = torch.Generator().manual_seed(w.seed + 100)
-    do = torch.randn(w.B, w.Sq, w.Hq, w.d, generator=g).to(torch.bfloat16)
-    dq, dk, dv = _run(q, k, v, do, w.causal, w.window, w.scale, cuda_device)
-    G = w.Hq // w.Hkv
-    for b, hk in ((0, 0), (w.B - 1, w.Hkv - 1)):
-        hs = slice(hk * G, (hk + 1) * G)
-        rq, rk, rv = oracle.bwd(q[b:b + 1, :, hs], k[b:b + 1, :, hk:hk + 1], v[b:b + 1, :, hk:hk + 1],
-                                do[b:b + 1, :, hs], causal=w.causal, window=w.window, scale=w.scale)
-        res = [_check_grad(a, r, f"{n} group ({b}, {hk})") for n, a, r in
-               (("dq", dq[b:b + 1, :, hs], rq), ("dk", dk[b:b + 1, :, hk:hk + 1], rk),
-                ("dv", dv[b:b + 1, :, hk:hk + 1], rv))]
-        _say(f"  group ({b}, {hk}) rel max/mean: " + " ".join(f"{m:.2e}/{e:.2e}" for m, e in res))

@@ -111,26 +111,6 @@ def test_int4_split_count_does_not_change_the_result(cuda_device):
         assert float((lse - outs[0][1]).abs().max()) <= 1e-4
 
 
-def test_full_size_int4_decode_sampled(cuda_device):
-    w = W.INT4_DECODE
-    _say(f"case: {w.name}")
-    q, kq, ks, vq, vs = W.decode_workload_inputs(w, device=cuda_device)
-    o, lse = fa.decode_int4(q, kq, ks, vq, vs, scale=w.scale, return_lse=True)
-    o2, lse2 = fa.decode_int4(q, kq, ks, vq, vs, scale=w.scale, return_lse=True)
-    torch.cuda.synchronize()
-    assert torch.equal(o, o2) and torch.equal(lse, lse2), "not bitwise repeatable"
-    rng = np.random.default_rng(w.seed)
-    rows = np.array([(0, 0), (w.B - 1, w.Hq - 1)] +
-                    [(rng.integers(w.B), rng.integers(w.Hq)) for _ in range(46)], dtype=np.int64)
-    qc, kqc, ksc, vqc, vsc = (t.cpu() for t in (q, kq, ks, vq, vs))
-    o_ref, lse_ref = oracle.decode_int4(qc, kqc, ksc, vqc, vsc, scale=w.scale, rows=rows)
-    o_np, l_np = _np64(o), _np64(lse)
-    o_got = np.stack([o_np[b, h] for b, h in rows])
-    l_got = np.array([l_np[b, h] for b, h in rows])
-    mx, mean = _check(o_got, o_ref, l_got, lse_ref, w.name)
-    _say(f"  sampled {len(rows)} rows: max-abs {mx:.3e} mean-abs {mean:.3e}")
-
-
 APPEND_CASES = [
     # B, T, Hkv, d, pos, cap, dtype
     (1, 1, 1, 64, 0, 1, torch.bfloat16),

@@ -1,10 +1,8 @@
 """GPU parity: libfattn (through its C ABI) against the fp64 oracle.
 
-Small and odd shapes are compared element by element over every output; the
-full-size workloads (run exactly as the benchmark launches them) are compared
-on sampled rows the oracle computes one by one, plus properties that hold at
-any size (every element finite and written, each output row inside the range
-of the values it averages, bitwise repeatability).
+Small and odd shapes are compared element by element over every output
+(outputs NaN-poisoned, so every element must be written); the full-size
+workloads are compared over every element in test_full_size_gpu.py.
 
 Tolerances (fixed for this build): fp32 inputs max-abs 1e-5 on o and lse;
 bf16 inputs max-abs 2e-2 and mean-abs 2e-3 on o, max-abs 1e-3 on lse.  The
@@ -60,19 +58,6 @@ def _run_fwd(q, k, v, causal, window, scale, dev):
 
 
 # ----------------------------------------------------------------- fp32 path
-
-def test_tiny_fp32_workload(cuda_device):
-    w = W.TINY_F32
-    _say(f"case: {w.name}")
-    q, k, v = W.workload_inputs(w)
-    o_ref, lse_ref = oracle.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale)
-    o, lse = _run_fwd(q.to(cuda_device), k.to(cuda_device), v.to(cuda_device), w.causal, w.window,
-                      w.scale, cuda_device)
-    err = np.abs(_np64(o) - o_ref).max()
-    lerr = np.abs(_np64(lse) - lse_ref).max()
-    _say(f"  max-abs o {err:.3e}, lse {lerr:.3e}")
-    assert err <= F32_TOL and lerr <= F32_TOL
-
 
 F32_CASES = [
     # B, Hq, Hkv, Sq, Skv, d, causal, window, scale
@@ -148,47 +133,6 @@ def test_bf16_odd_shapes(case, cuda_device):
     _say(f"  max-abs {mx:.3e} mean-abs {mean:.3e}")
 
 
-def _sample_rows(B, Hq, Sq, n, seed):
-    """(b, h, i) rows: first/last positions, tile edges, and random ones."""
-    rng = np.random.default_rng(seed)
-    edges = [0, 1, 31, 32, 63, 64, 127, 128, 129, 511, 512, 1023, Sq // 2, Sq - 2, Sq - 1]
-    rows = []
-    for i in edges:
-        if 0 <= i < Sq:
-            rows.append((rng.integers(B), rng.integers(Hq), i))
-    for h in range(Hq):  # every head at least once
-        rows.append((rng.integers(B), h, rng.integers(Sq)))
-    while len(rows) < n:
-        rows.append((rng.integers(B), rng.integers(Hq), rng.integers(Sq)))
-    return np.array(rows, dtype=np.int64)
-
-
-FULL = [W.MHA_CAUSAL, W.GQA_CAUSAL, W.MQA_CAUSAL, W.MQA_WINDOW]
-
-
-@pytest.mark.parametrize("w", FULL, ids=[w.name for w in FULL])
-def test_full_size_prefill_sampled(w, cuda_device):
-    _say(f"case: {w.name}")
-    q, k, v = W.workload_inputs(w)
-    qd, kd, vd = q.to(cuda_device), k.to(cuda_device), v.to(cuda_device)
-    o, lse = _run_fwd(qd, kd, vd, w.causal, w.window, w.scale, cuda_device)
-    o2, lse2 = _run_fwd(qd, kd, vd, w.causal, w.window, w.scale, cuda_device)
-    assert torch.equal(o, o2) and torch.equal(lse, lse2), "not bitwise repeatable"
-    assert bool(torch.isfinite(o).all()), "non-finite (or unwritten) output"
-    assert bool(torch.isfinite(lse).all())
-    rows = _sample_rows(w.B, w.Hq, w.Sq, 384, seed=w.seed)
-    o_ref, lse_ref = oracle.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale, rows=rows)
-    o_np = o.float().cpu().numpy()
-    l_np = lse.cpu().numpy()
-    o_got = np.stack([o_np[b, i, h] for b, h, i in rows]).astype(np.float64)
-    l_got = np.array([l_np[b, h, i] for b, h, i in rows], dtype=np.float64)
-    mx, mean = _check_bf16(o_got, o_ref, l_got, lse_ref, w.name)
-    _say(f"  sampled {len(rows)} rows: max-abs {mx:.3e} mean-abs {mean:.3e}")
-    # any size: each output row is a convex combination of the visible V rows
-    vmax = v.float().abs().amax().item()
-    assert float(o.float().abs().amax()) <= vmax * (1 + 2 ** -7) + 1e-6
-
-
 # -------------------------------------------------------------------- decode
 
 DECODE_CASES = [
@@ -244,24 +188,3 @@ def test_decode_split_count_does_not_change_the_result(cuda_device):
     for o, lse in outs[1:]:
         assert float((o - outs[0][0]).abs().max()) <= 2 ** -7
         assert float((lse - outs[0][1]).abs().max()) <= 1e-4
-
-
-def test_full_size_decode_sampled(cuda_device):
-    w = W.INT8_DECODE
-    _say(f"case: {w.name}")
-    q, kq, ks, vq, vs = W.decode_workload_inputs(w, device=cuda_device)
-    o, lse = fa.decode_int8(q, kq, ks, vq, vs, scale=w.scale, return_lse=True)
-    o2, lse2 = fa.decode_int8(q, kq, ks, vq, vs, scale=w.scale, return_lse=True)
-    torch.cuda.synchronize()
-    assert torch.equal(o, o2) and torch.equal(lse, lse2), "not bitwise repeatable"
-    assert bool(torch.isfinite(o.float()).all())
-    rng = np.random.default_rng(w.seed)
-    rows = np.array([(0, 0), (w.B - 1, w.Hq - 1)] +
-                    [(rng.integers(w.B), rng.integers(w.Hq)) for _ in range(46)], dtype=np.int64)
-    qc, kqc, ksc, vqc, vsc = (t.cpu() for t in (q, kq, ks, vq, vs))
-    o_ref, lse_ref = oracle.decode_int8(qc, kqc, ksc, vqc, vsc, scale=w.scale, rows=rows)
-    o_np, l_np = _np64(o), _np64(lse)
-    o_got = np.stack([o_np[b, h] for b, h in rows])
-    l_got = np.array([l_np[b, h] for b, h in rows])
-    mx, mean = _check_bf16(o_got, o_ref, l_got, lse_ref, w.name)
-    _say(f"  sampled {len(rows)} rows: max-abs {mx:.3e} mean-abs {mean:.3e}")
