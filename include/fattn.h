@@ -15,11 +15,16 @@
  * device data such as the varlen lengths is read at each replay.
  *
  * Every device pointer must be 16-byte aligned (allocator-returned pointers
- * are); a misaligned pointer is rejected with FATTN_EINVAL.
+ * are), except cu_seqlens_q/k, seqlens and the lse of fattn_fwd_varlen,
+ * which need 4 bytes; a misaligned pointer is rejected with FATTN_EINVAL.
  *
  * Errors: arguments are validated before any HIP call is made.  On any
  * FATTN_E* status except FATTN_EHIP nothing has been enqueued and no output
- * has been written.  FATTN_EHIP reports a failed kernel launch.
+ * has been written.  FATTN_EHIP means that the HIP runtime refused one of
+ * this call's own kernel launches (the status that launch returned); the
+ * launches after it were not enqueued.  The library never calls
+ * hipGetLastError: an error left pending by the caller's earlier HIP calls
+ * is not reported by, and not cleared by, a libfattn call.
  *
  * Sources, cited by page title and section:
  *  [FA-NPU]      "When Transformer meets the Ascend NPU: the memory-slimming
@@ -116,7 +121,11 @@ FATTN_API int fattn_fwd(const void* q, const void* k, const void* v, void* o, fl
  *        0 to total_q / total_k.  They live on the device and are not checked
  *        on the host: offsets out of range are clamped into the tensors (the
  *        kernels never address outside them) but give unspecified results.
- * max_seqlen_q  >= every Sq_b (rows past it are not computed); <= total_q.
+ * max_seqlen_q  the longest Sq_b; it sizes the grid; <= total_q.  If a
+ *        sequence is longer, its rows at positions >= max_seqlen_q may be
+ *        left unwritten; every row that is written is exact for the
+ *        sequence's true lengths (its causal diagonal still ends at its
+ *        last key).
  * total_q = 0 is a valid empty call.  Other rules and errors as fattn_fwd.
  */
 FATTN_API int fattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -165,10 +174,13 @@ FATTN_API size_t fattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk
  * code * scale.  The kernel reads the codes from HBM and converts them in
  * registers, folding the scales into the scores and the probabilities.
  * The keys are cut into splits processed in parallel, each producing a
- * partial (o_s, lse_s) in the workspace; a second kernel merges them by
- * log-sum-exp (the local-max-and-sum correction of the [FA-NPU] tiling
- * section applied across splits).  With a single split the output is
- * written directly and the merge kernel is not launched.
+ * partial (o_s, lse_s), and the partials are merged by log-sum-exp (the
+ * local-max-and-sum correction of the [FA-NPU] tiling section applied across
+ * splits).  With at most 8 splits the splits of a (b, kv head) stream share
+ * one workgroup, which merges them on chip: one kernel launch, and the
+ * workspace is not touched.  With more, the partials go to the workspace and
+ * a second kernel merges them.  With a single split the output is written
+ * directly.  Every form gives the same bits for the same split count.
  *
  * q          [B, Hq, d] bf16          (the [B, 1, Hq, d] query of the new token)
  * kq, vq     [B, Hkv, Skv, d] int8    (head-major cache: one contiguous stream

@@ -128,6 +128,7 @@ def _fwd(**kw):
 @pytest.mark.parametrize("kw,want", [
     (dict(q=None), FATTN_EINVAL), (dict(k=None), FATTN_EINVAL), (dict(v=None), FATTN_EINVAL),
     (dict(o=None), FATTN_EINVAL), (dict(q=P + 8), FATTN_EINVAL), (dict(o=P + 2), FATTN_EINVAL),
+    (dict(lse=P + 4), FATTN_EINVAL), (dict(lse=P + 8), FATTN_EINVAL),
     (dict(B=0), FATTN_EINVAL), (dict(Hq=0), FATTN_EINVAL), (dict(Hkv=0), FATTN_EINVAL),
     (dict(Sq=0), FATTN_EINVAL), (dict(Skv=-1), FATTN_EINVAL), (dict(d=0), FATTN_EINVAL),
     (dict(Hq=3, Hkv=2), FATTN_EINVAL), (dict(scale=math.inf), FATTN_EINVAL),

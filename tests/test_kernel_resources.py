@@ -24,10 +24,15 @@ MIN_OCCUPANCY = {
     "fwd_bf16_kernel<128>": 2,
     "fwd_f32_kernel<64>": 2,
     "fwd_f32_kernel<128>": 1,
-    "decode_split_kernel<64,8>": 3,
-    "decode_split_kernel<64,4>": 4,
-    "decode_split_kernel<128,8>": 2,
-    "decode_split_kernel<128,4>": 2,
+    # <D, code bits, workgroup form>
+    "decode_split_kernel<64,8,0>": 3,
+    "decode_split_kernel<64,4,0>": 4,
+    "decode_split_kernel<128,8,0>": 2,
+    "decode_split_kernel<128,4,0>": 2,
+    "decode_split_kernel<64,8,1>": 3,
+    "decode_split_kernel<64,4,1>": 4,
+    "decode_split_kernel<128,8,1>": 2,
+    "decode_split_kernel<128,4,1>": 2,
     "decode_merge_kernel<64>": 8,
     "decode_merge_kernel<128>": 8,
     "bwd_pre_kernel<64>": 8,
@@ -47,7 +52,7 @@ def _short_name(mangled: str) -> str:
     name = m.group(1)
     if name == "kv_quant_kernel" or name == "bwd_reduce_kernel":
         return name
-    ints = re.findall(r"Li(\d+)E", mangled)
+    ints = re.findall(r"L[ib](\d+)E", mangled)  # int and bool template arguments
     return f"{name}<{','.join(ints)}>"
 
 

@@ -716,15 +716,19 @@ int heads_per_chunk_shift(int G) {
 template <int D>
 hipError_t launch_all(const BwdParams& p, int64_t pre_blocks, int64_t dq_blocks, int64_t kv_blocks,
                       hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(unsigned(pre_blocks)), dim3(256), 0, stream, p);
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(unsigned(dq_blocks)), dim3(kThreads), 0, stream, p);
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(unsigned(kv_blocks)), dim3(kThreads), 0, stream, p);
-  if (p.nsplit > 1) {
+  // each kernel reads what the previous ones wrote: stop at the first
+  // launch that fails, so none runs on a workspace that was never filled
+  hipError_t err = launch_kernel(bwd_pre_kernel<D>, dim3(unsigned(pre_blocks)), dim3(256), 0, stream, p);
+  if (err == hipSuccess)
+    err = launch_kernel(bwd_dq_kernel<D>, dim3(unsigned(dq_blocks)), dim3(kThreads), 0, stream, p);
+  if (err == hipSuccess)
+    err = launch_kernel(bwd_dkdv_kernel<D>, dim3(unsigned(kv_blocks)), dim3(kThreads), 0, stream, p);
+  if (err == hipSuccess && p.nsplit > 1) {
     const int64_t n = int64_t(p.B) * p.Skv * p.Hkv * D;
     const int64_t blocks = (n / 8 + 255) / 256;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p, n);
+    err = launch_kernel(bwd_reduce_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, p, n);
   }
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace

@@ -8,10 +8,14 @@
 // scale) and to the probabilities (v scale).  The keys of each
 // (batch, kv head) stream are cut into splits; each split runs the online
 // softmax of the [FA-NPU] tiling section over its tokens and writes a
-// normalised partial output and its log-sum-exp; a second kernel merges the
-// partials (global max of the partial lse, weights e^(lse_s - max)).  With a
-// single split the split kernel writes the output and lse itself and the
-// merge is not launched (its result would be the same bits).
+// normalised partial output and its log-sum-exp, and the partials are merged
+// by log-sum-exp (global max of the partial lse, weights e^(lse_s - max)).
+// Where a stream has at most kWgMaxSplits splits, its splits are the waves of
+// one workgroup, which merges them in LDS after a barrier and writes the
+// output: one launch, no partials in memory.  More splits than that write
+// partials to the workspace and a second kernel merges them.  With a single
+// split the split kernel writes the output and lse itself.  All three forms
+// do the same arithmetic in the same order, so they give the same bits.
 //
 // gfx950 design (split kernel): one wave per (batch, kv head, chunk of <= 16
 // query heads, split).  Per 32-token tile:
@@ -62,6 +66,10 @@ constexpr float kLazy = 8.f;         // N of the 16x16x32 product
 
 static_assert(kDecodeTile % kTile == 0, "split chunks must hold whole tiles");
 
+// Most splits one workgroup can hold: one wave per split at two waves per
+// SIMD (the split kernel's register budget) on the four SIMDs of a CU.
+constexpr int kWgMaxSplits = 8;
+
 struct SplitParams {
   const __bf16* q;
   const uint8_t* kq;
@@ -92,7 +100,24 @@ struct Geom {
   static constexpr int VLOADS = kTile / RPL;      // 16-byte V loads per lane per tile
   static constexpr int VSTRIDE = RB + 16;         // padded LDS row (bytes)
   static constexpr int NREAD = RB / 16;           // transposed V reads per tile
+  // LDS of one wave: the staged V tile, then the tile's k and v scales
+  static constexpr int WAVE_LDS = kTile * VSTRIDE + 2 * kTile * 4;
+  // merge area of the workgroup form: partial outputs [split][head][D + 4]
+  // (rows padded by 16 bytes so the 16 heads of a 16-byte store hit
+  // different banks), then partial lse [split][head]
+  static constexpr int MROW = D + 4;
 };
+
+// Dynamic LDS bytes of a split-kernel block of nw waves (nw > 1: the
+// workgroup form, whose merge area reuses the waves' staging areas).
+template <int D, int BITS>
+constexpr size_t split_lds_bytes(int nw, int heads) {
+  using GM = Geom<D, BITS>;
+  const size_t stage = size_t(nw) * GM::WAVE_LDS;
+  if (nw == 1) return stage;
+  const size_t merge = size_t(nw) * heads * (GM::MROW + 1) * 4;
+  return stage > merge ? stage : merge;
+}
 
 // bf16 of (136 + code) for 8 int4 codes: element e of lo4 / hi4 is the code
 // in the low nibble of byte e (already 0 .. 15 = code + 8).  The two results'
@@ -138,8 +163,11 @@ struct TileRegs {
   float sc;  // lane l < 32: k scale of token l; lane l >= 32: v scale of token l - 32
 };
 
-template <int D, int BITS>
-__global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
+// WG = false: one wave per block, block id = ((b * Hkv + hk) * nhc + hc) *
+// nsplit + split.  WG = true: one block per (b, hk, hc) with one wave per
+// split (nsplit <= kWgMaxSplits waves), merged in LDS.
+template <int D, int BITS, bool WG>
+__global__ __launch_bounds__(WG ? 64 * kWgMaxSplits : 64, 2) void decode_split_kernel(SplitParams p) {
   using GM = Geom<D, BITS>;
   constexpr int RB = GM::RB;
   constexpr int KB = GM::KB;
@@ -149,15 +177,23 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   constexpr int RPL = GM::RPL;
   constexpr int VSTRIDE = GM::VSTRIDE;
   constexpr int CB = D / 16;              // 16-dim blocks of the output (= products per tile)
-  __shared__ __attribute__((aligned(16))) char vlds[kTile * VSTRIDE];
-  __shared__ __attribute__((aligned(16))) float slds[2 * kTile];   // k scales, then v scales
+  extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+  const int wave = WG ? int(threadIdx.x >> 6) : 0;
+  char* const vlds = dyn_lds + wave * GM::WAVE_LDS;                         // staged V codes
+  float* const slds = reinterpret_cast<float*>(vlds + kTile * VSTRIDE);  // k scales, then v scales
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15;   // head slot (B/C column), also token row of A
   const int g = lane >> 4;   // lane group
 
   int id = blockIdx.x;
-  const int split = id % p.nsplit; id /= p.nsplit;
+  int split;
+  if constexpr (WG) {
+    split = wave;
+  } else {
+    split = id % p.nsplit;
+    id /= p.nsplit;
+  }
   const int hc = id % p.nhc; id /= p.nhc;
   const int hk = id % p.Hkv;
   const int b = id / p.Hkv;
@@ -373,10 +409,10 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
   // row sum over the four lane groups holding this head's tokens
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (!head_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_row = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
   if (p.nsplit == 1) {
+    if (!head_ok) return;
     // a single split is the whole row: write the bf16 output and lse here
     // (what the merge would produce: weight exp(0) = 1, log 1 = 0)
     __bf16* orow = p.o + (int64_t(b) * p.Hq + hq) * D;
@@ -399,25 +435,69 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(SplitParams p) {
     if (g == 0 && p.lse) p.lse[int64_t(b) * p.Hq + hq] = lse_row;
     return;
   }
-  const int64_t prow = (int64_t(b) * p.Hq + hq) * p.nsplit + split;
-  float* po = p.part_o + prow * D;
-  if constexpr (BITS == 8) {
+
+  // the normalised partial output of this split, written as 4-float pieces:
+  // put(dim, f32x4) stores output dims dim .. dim+3 of head slot n
+  auto write_partial = [&](auto put) __attribute__((always_inline)) {
+    if constexpr (BITS == 8) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      // acc[cb][r] holds output dim 16*cb + 4g + r of head slot n
-      *reinterpret_cast<f32x4*>(po + 16 * cb + 4 * g) = acc[cb] * inv;
+      for (int cb = 0; cb < CB; ++cb) put(16 * cb + 4 * g, acc[cb] * inv);  // dims 16cb + 4g + r
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < GM::NREAD; ++cb) {
+        // acc[2cb][r] / acc[2cb+1][r]: dims 32*cb + 8g + 2r and that + 1, each
+        // carrying the bias 136 * sum(p') that pbias holds in every register
+        const f32x4 e = (acc[2 * cb] - pbias) * inv, o = (acc[2 * cb + 1] - pbias) * inv;
+        put(32 * cb + 8 * g, f32x4{e[0], o[0], e[1], o[1]});
+        put(32 * cb + 8 * g + 4, f32x4{e[2], o[2], e[3], o[3]});
+      }
     }
+  };
+
+  if constexpr (WG) {
+    // Workgroup form: every wave (split) of the block leaves its partial in
+    // LDS, over the staging areas (the barrier guarantees that no wave still
+    // reads them), and the block merges in split order with the arithmetic
+    // of decode_merge_kernel.
+    const int hpw = min(kHeadsPerWave, p.G);  // head slots the merge area holds
+    float* const mo = reinterpret_cast<float*>(dyn_lds);
+    float* const ml = mo + p.nsplit * hpw * GM::MROW;
+    __syncthreads();
+    if (head_ok) {
+      float* row = mo + (split * hpw + n) * GM::MROW;
+      write_partial([&](int dim, const f32x4& v) __attribute__((always_inline)) {
+        *reinterpret_cast<f32x4*>(row + dim) = v;
+      });
+      if (g == 0) ml[split * hpw + n] = lse_row;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nheads * D; idx += blockDim.x) {
+      const int h = idx / D, c = idx % D;
+      float mx = -INFINITY;
+      for (int s2 = 0; s2 < p.nsplit; ++s2) mx = fmaxf(mx, ml[s2 * hpw + h]);
+      float a = 0.f, wsum = 0.f;
+      if (mx != -INFINITY) {
+        for (int s2 = 0; s2 < p.nsplit; ++s2) {
+          const float wgt = expf(ml[s2 * hpw + h] - mx);  // 0 for an empty split
+          wsum += wgt;
+          a = fmaf(wgt, mo[(s2 * hpw + h) * GM::MROW + c], a);
+        }
+      }
+      const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+      const int64_t orow = int64_t(b) * p.Hq + hk * p.G + head0 + h;
+      p.o[orow * D + c] = (__bf16)(a * winv);
+      if (c == 0 && p.lse) p.lse[orow] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
+    }
+    return;
   } else {
-#pragma unroll
-    for (int cb = 0; cb < GM::NREAD; ++cb) {
-      // acc[2cb][r] / acc[2cb+1][r]: dims 32*cb + 8g + 2r and that + 1, each
-      // carrying the bias 136 * sum(p') that pbias holds in every register
-      const f32x4 e = (acc[2 * cb] - pbias) * inv, o = (acc[2 * cb + 1] - pbias) * inv;
-      *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
-      *reinterpret_cast<f32x4*>(po + 32 * cb + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
-    }
+    if (!head_ok) return;
+    const int64_t prow = (int64_t(b) * p.Hq + hq) * p.nsplit + split;
+    float* po = p.part_o + prow * D;
+    write_partial([&](int dim, const f32x4& v) __attribute__((always_inline)) {
+      *reinterpret_cast<f32x4*>(po + dim) = v;
+    });
+    if (g == 0) p.part_lse[prow] = lse_row;
   }
-  if (g == 0) p.part_lse[prow] = lse_row;
 }
 
 // One wave per (batch, query head): merges nsplit partials by log-sum-exp.
@@ -454,12 +534,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restric
 }
 
 template <int D, int BITS>
-void launch_split_and_merge(const DecodeArgs& a, const SplitParams& p, unsigned waves,
-                            unsigned rows, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, BITS>), dim3(waves), dim3(64), 0, stream, p);
-  if (a.nsplit > 1)  // one split writes the output itself
-    hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(rows), dim3(64), 0, stream,
-                       a.part_o, a.part_lse, static_cast<__bf16*>(a.o), a.lse, a.nsplit);
+hipError_t launch_split_and_merge(const DecodeArgs& a, const SplitParams& p, hipStream_t stream) {
+  const int64_t groups = int64_t(a.B) * a.Hkv * p.nhc;  // (b, kv head, head chunk)
+  if (a.nsplit > 1 && a.nsplit <= kWgMaxSplits) {
+    const int hpw = p.G < kHeadsPerWave ? p.G : kHeadsPerWave;
+    return launch_kernel(decode_split_kernel<D, BITS, true>, dim3(unsigned(groups)),
+                         dim3(64 * a.nsplit), split_lds_bytes<D, BITS>(a.nsplit, hpw), stream, p);
+  }
+  hipError_t err = launch_kernel(decode_split_kernel<D, BITS, false>,
+                                 dim3(unsigned(groups * a.nsplit)), dim3(64),
+                                 split_lds_bytes<D, BITS>(1, 0), stream, p);
+  if (err != hipSuccess || a.nsplit == 1) return err;  // one split writes the output itself
+  return launch_kernel(decode_merge_kernel<D>, dim3(unsigned(int64_t(a.B) * a.Hq)), dim3(64), 0,
+                       stream, a.part_o, a.part_lse, static_cast<__bf16*>(a.o), a.lse, a.nsplit);
 }
 
 }  // namespace
@@ -488,15 +575,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = int64_t(a.B) * a.Hq;
   if (waves > 0x7fffffff || rows > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.bits != 8 && a.bits != 4) return hipErrorInvalidValue;
-  const unsigned w = unsigned(waves), r = unsigned(rows);
   if (a.d == 64) {
-    if (a.bits == 8) launch_split_and_merge<64, 8>(a, p, w, r, stream);
-    else launch_split_and_merge<64, 4>(a, p, w, r, stream);
-  } else {
-    if (a.bits == 8) launch_split_and_merge<128, 8>(a, p, w, r, stream);
-    else launch_split_and_merge<128, 4>(a, p, w, r, stream);
+    return a.bits == 8 ? launch_split_and_merge<64, 8>(a, p, stream)
+                       : launch_split_and_merge<64, 4>(a, p, stream);
   }
-  return hipGetLastError();
+  return a.bits == 8 ? launch_split_and_merge<128, 8>(a, p, stream)
+                     : launch_split_and_merge<128, 4>(a, p, stream);
 }
 
 }  // namespace fattn

@@ -161,8 +161,11 @@ __device__ __forceinline__ void store_tile_rows_bf16(char* stage, const f32x16* 
 
 // Rows and lengths of one sequence: dense batches index b * S; packed batches
 // read the cumulative offsets, clamped so that no value can address memory
-// outside the packed tensors (Sq of a packed batch is the longest query
-// sequence, Skv is unused).
+// outside the packed tensors.  For a packed batch the Sq argument is the
+// caller's bound on the query lengths, which sizes the grid only: the
+// returned Sq is the sequence's own length, so the causal diagonal (offset
+// Skv_b - Sq_b) stays right for a sequence longer than that bound, whose
+// rows past the grid are then simply not computed (Skv is unused).
 struct SeqView {
   int Sq, Skv;
   int64_t q_row0, k_row0;   // first packed row of the sequence
@@ -183,7 +186,7 @@ __device__ __forceinline__ SeqView seq_view(const int* cu_q, const int* cu_k, in
   }
   const int q0 = min(max(cu_q[b], 0), total_q), q1 = min(max(cu_q[b + 1], q0), total_q);
   const int k0 = min(max(cu_k[b], 0), total_k), k1 = min(max(cu_k[b + 1], k0), total_k);
-  s.Sq = min(q1 - q0, Sq);  // the grid covers Sq (the longest sequence) rows
+  s.Sq = q1 - q0;
   s.Skv = k1 - k0;
   s.q_row0 = q0;
   s.k_row0 = k0;

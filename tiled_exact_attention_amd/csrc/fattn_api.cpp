@@ -155,6 +155,7 @@ int fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
               float scale, int causal, int window, int dtype, void* stream) {
   if (!q || !k || !v || !o) return FATTN_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FATTN_EINVAL;
+  if (lse && !aligned16(lse)) return FATTN_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || d < 1) return FATTN_EINVAL;
   if (Hq % Hkv != 0) return FATTN_EINVAL;
   if (!std::isfinite(scale)) return FATTN_EINVAL;

@@ -487,12 +487,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.total_k = a.total_k;
   const int64_t blocks = int64_t(p.nqb) * p.nx;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.d == 64) {
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
-  }
-  return hipGetLastError();
+  return launch_kernel(a.d == 64 ? fwd_bf16_kernel<64> : fwd_bf16_kernel<128>,
+                       dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
 }
 
 }  // namespace fattn

@@ -165,16 +165,9 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
   const float* k = static_cast<const float*>(a.k);
   const float* v = static_cast<const float*>(a.v);
   float* o = static_cast<float*>(a.o);
-  if (a.d == 64) {
-    hipLaunchKernelGGL(fwd_f32_kernel<64>, grid, dim3(64), 0, stream, q, k, v, o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, a.causal, a.window, a.cu_q, a.cu_k,
-                       a.total_q, a.total_k);
-  } else {
-    hipLaunchKernelGGL(fwd_f32_kernel<128>, grid, dim3(64), 0, stream, q, k, v, o, a.lse,
-                       a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, a.causal, a.window, a.cu_q, a.cu_k,
-                       a.total_q, a.total_k);
-  }
-  return hipGetLastError();
+  return launch_kernel(a.d == 64 ? fwd_f32_kernel<64> : fwd_f32_kernel<128>, grid, dim3(64), 0,
+                       stream, q, k, v, o, a.lse, a.Hq, a.Hkv, a.Sq, a.Skv, a.scale, a.causal,
+                       a.window, a.cu_q, a.cu_k, a.total_q, a.total_k);
 }
 
 }  // namespace fattn

@@ -126,10 +126,9 @@ hipError_t launch_idx(const KvQuantArgs& a, int64_t rows, hipStream_t stream) {
   constexpr int RPB = kThreads / (D / 8) * kRows;
   const int64_t blocks = (rows + RPB - 1) / RPB;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((kv_quant_kernel<D, T, I, BITS>), dim3(unsigned(blocks)), dim3(kThreads), 0,
-                     stream, static_cast<const T*>(a.x), static_cast<uint8_t*>(a.codes), a.scales,
-                     rows, a.T, a.Hkv, a.pos, a.cap);
-  return hipGetLastError();
+  return launch_kernel(kv_quant_kernel<D, T, I, BITS>, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                       stream, static_cast<const T*>(a.x), static_cast<uint8_t*>(a.codes), a.scales,
+                       rows, a.T, a.Hkv, a.pos, a.cap);
 }
 
 template <int D, typename T, int BITS>

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <tuple>
 
 namespace fattn {
 
@@ -89,5 +90,22 @@ hipError_t launch_kv_quant(const KvQuantArgs& a, hipStream_t stream);
 
 // Key-tile length of the decode split kernel; split chunks are multiples of it.
 constexpr int kDecodeTile = 64;
+
+// Enqueues kernel<<<grid, block, lds, stream>>>(args...) and returns the
+// status of that launch itself (hipLaunchKernel's result), never an error
+// left pending by an earlier HIP call: the library does not call
+// hipGetLastError, so such an error is neither reported nor consumed here.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds,
+                         hipStream_t stream, A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "argument count");
+  auto typed = std::make_tuple(P(args)...);
+  void* ptrs[sizeof...(P)];
+  std::apply([&](auto&... x) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&x)), ...);
+  }, typed);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream);
+}
 
 }  // namespace fattn
