@@ -202,6 +202,30 @@ FATTN_API int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_
                       void* stream);
 
 /*
+ * fattn_decode_int8 for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops and harnesses that forbid
+ * hipMalloc.  Same operation, arguments (without the workspace), split plan
+ * and results, bit for bit.  Plans that merge through partials (more than 8
+ * splits per (b, kv head) stream) keep them in a scratch array built into the
+ * library instead of a caller workspace: 32 MiB per GPU, allocated when the
+ * library's code is loaded on that GPU and held until the process ends; with
+ * at most 8 splits nothing beyond o and lse is touched.  Besides its kernel
+ * launches the call makes hipGetDevice and, on its first use of a device,
+ * hipGetSymbolAddress; it allocates nothing.  Every call on one GPU shares
+ * that GPU's scratch, which keeps the last call's contents (nothing in it has
+ * to start at zero): calls that use it and overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.
+ *
+ * Errors as fattn_decode_int8, plus FATTN_EWORKSPACE when the plan's partials
+ * (fattn_decode_workspace_size for the same arguments) exceed the 32 MiB, and
+ * FATTN_EHIP when the scratch address cannot be obtained on the current device.
+ */
+FATTN_API int fattn_decode_int8_noalloc(const void* q, const int8_t* kq, const float* k_scale,
+                      const int8_t* vq, const float* v_scale, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Skv, int d, float scale,
+                      int num_splits, void* stream);
+
+/*
  * Decode over an int4 KV cache: the same operation, arguments, split plan,
  * workspace size and error behaviour as fattn_decode_int8, with the cache
  * compressed one step further ([FA-3MOVES] move 3 taken to 4-bit codes; the

@@ -47,7 +47,7 @@ def test_library_is_built_and_loads():
 def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert names == sorted(["fattn_fwd", "fattn_fwd_varlen", "fattn_bwd", "fattn_bwd_workspace_size",
-                            "fattn_decode_int8", "fattn_decode_int4",
+                            "fattn_decode_int8", "fattn_decode_int4", "fattn_decode_int8_noalloc",
                             "fattn_decode_int8_varlen", "fattn_decode_int4_varlen",
                             "fattn_decode_num_splits", "fattn_decode_workspace_size",
                             "fattn_kv_append_int8", "fattn_kv_append_int4",
@@ -304,3 +304,34 @@ def test_bwd_workspace_size_rejects_bad_arguments():
     if not _gpu_visible():
         need = fa.fattn_bwd_workspace_size(1, 4, 2, 8, 8, 64)
         assert _bwd(ws_bytes=need - 1) == FATTN_EWORKSPACE
+
+
+def _dec_noalloc(**kw):
+    a = dict(q=P, kq=P, ks=P, vq=P, vs=P, o=P, lse=None, B=1, Hq=4, Hkv=2, Skv=100, d=128,
+             scale=0.1, num_splits=0, stream=None)
+    a.update(kw)
+    return fa.fattn_decode_int8_noalloc(a["q"], a["kq"], a["ks"], a["vq"], a["vs"], a["o"], a["lse"],
+                                        a["B"], a["Hq"], a["Hkv"], a["Skv"], a["d"], a["scale"],
+                                        a["num_splits"], a["stream"])
+
+
+@no_gpu_only
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=None), FATTN_EINVAL), (dict(vs=None), FATTN_EINVAL), (dict(lse=P + 4), FATTN_EINVAL),
+    (dict(Hq=3), FATTN_EINVAL), (dict(num_splits=-1), FATTN_EINVAL), (dict(d=32), FATTN_EUNSUPPORTED),
+    # partials of 1024 heads x 1000 splits x (128 + 1) floats: beyond the built-in 32 MiB
+    (dict(Hq=1024, Hkv=1, Skv=1 << 20, num_splits=1000), FATTN_EWORKSPACE),
+])
+def test_decode_noalloc_rejects_before_any_device_work(kw, want):
+    assert _dec_noalloc(**kw) == want
+
+
+@no_gpu_only
+def test_decode_noalloc_scratch_limit_is_the_workspace_size():
+    # the built-in scratch holds 32 MiB: a plan whose workspace size is just
+    # above it is rejected before any device work; the one below it fits
+    limit = 32 << 20
+    big = dict(Hq=1024, Hkv=1, Skv=1 << 20)
+    assert fa.decode_workspace_size(1, 1024, 1, 1 << 20, 128, 64) > limit
+    assert _dec_noalloc(num_splits=64, **big) == FATTN_EWORKSPACE
+    assert fa.decode_workspace_size(1, 1024, 1, 1 << 20, 128, 63) <= limit

@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     fattn_decode_int4,
     fattn_decode_int4_varlen,
     fattn_decode_int8,
+    fattn_decode_int8_noalloc,
     fattn_decode_int8_varlen,
     fattn_decode_num_splits,
     fattn_decode_workspace_size,

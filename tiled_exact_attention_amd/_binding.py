@@ -2,7 +2,7 @@
 
 The raw entry points (``fattn_fwd``, ``fattn_fwd_varlen``, ``fattn_bwd``,
 ``fattn_bwd_workspace_size``, ``fattn_decode_int8``,
-``fattn_decode_int4``, their ``_varlen`` forms, ``fattn_kv_append_int8``,
+``fattn_decode_int4``, their ``_varlen`` forms, ``fattn_decode_int8_noalloc``, ``fattn_kv_append_int8``,
 ``fattn_kv_append_int4``,
 ``fattn_decode_workspace_size``, ``fattn_decode_num_splits``,
 ``fattn_status_string``, ``fattn_version``) have the C names and take plain
@@ -55,6 +55,9 @@ def load():
         lib.fattn_decode_int8.restype = i32
         lib.fattn_decode_int4.argtypes = lib.fattn_decode_int8.argtypes
         lib.fattn_decode_int4.restype = i32
+        lib.fattn_decode_int8_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                  f32, i32, vp]
+        lib.fattn_decode_int8_noalloc.restype = i32
         lib.fattn_bwd.argtypes = [vp] * 9 + [i32] * 6 + [f32, i32, i32, i32, vp, sz, vp]
         lib.fattn_bwd.restype = i32
         lib.fattn_bwd_workspace_size.argtypes = [i32] * 6
@@ -92,6 +95,12 @@ def fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, s
                       num_splits, workspace, workspace_bytes, stream) -> int:
     return load().fattn_decode_int8(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d,
                                     scale, num_splits, workspace, workspace_bytes, stream)
+
+
+def fattn_decode_int8_noalloc(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
+                              num_splits, stream) -> int:
+    return load().fattn_decode_int8_noalloc(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d,
+                                            scale, num_splits, stream)
 
 
 def fattn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Skv, d, scale, causal, window,

@@ -51,6 +51,7 @@
 #include "launch.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace fattn {
 namespace {
@@ -68,7 +69,8 @@ static_assert(kDecodeTile % kTile == 0, "split chunks must hold whole tiles");
 
 // Most splits one workgroup can hold: one wave per split at two waves per
 // SIMD (the split kernel's register budget) on the four SIMDs of a CU.
-constexpr int kWgMaxSplits = 8;
+constexpr int kWgMaxSplits = kDecodeWgMaxSplits;
+static_assert(kWgMaxSplits * 64 <= 1024, "a workgroup holds at most 16 waves");
 
 struct SplitParams {
   const __bf16* q;
@@ -550,6 +552,38 @@ hipError_t launch_split_and_merge(const DecodeArgs& a, const SplitParams& p, hip
 }
 
 }  // namespace
+
+// ---- built-in scratch for callers that cannot allocate.  The partial
+// outputs and lse of plans that merge in a second kernel go here instead of
+// a caller workspace (fattn_decode_int8_noalloc).  Nothing in it needs to
+// start at zero: every partial is written before the merge reads it.  Every
+// call on one GPU uses that GPU's copy, so calls that overlap on a GPU race.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once taken
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // the array's name is a host-side stand-in: only this address may be
+    // handed to kernels (each device holds its own copy at its own address)
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   SplitParams p;

@@ -107,6 +107,10 @@ size_t workspace_bytes_for(int B, int Hq, int nsplit, int d) {
   return o_bytes + rows * sizeof(float);
 }
 
+// workspace == kBuiltinScratch: the library's own scratch array instead of a
+// caller workspace (fattn_decode_int8_noalloc).
+void* const kBuiltinScratch = reinterpret_cast<void*>(uintptr_t(1));
+
 int decode(const void* q, const void* kq, const float* k_scale, const void* vq,
            const float* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Skv, int d,
            float scale, int num_splits, void* workspace, size_t workspace_bytes, void* stream,
@@ -115,18 +119,28 @@ int decode(const void* q, const void* kq, const float* k_scale, const void* vq,
                            num_splits, true);
   if (st != FATTN_OK) return st;
   if (varlen && (!seqlens || !aligned4(seqlens))) return FATTN_EINVAL;
+  if (lse && !aligned16(lse)) return FATTN_EINVAL;
   int nsplit, chunk;
   plan_splits(B, Hq, Hkv, Skv, num_splits, &nsplit, &chunk);
   size_t need = workspace_bytes_for(B, Hq, nsplit, d);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FATTN_EWORKSPACE;
-  if (lse && !aligned16(lse)) return FATTN_EINVAL;
+  if (workspace == kBuiltinScratch) {
+    if (need > fattn::kDecodeScratchBytes) return FATTN_EWORKSPACE;
+    // only plans that merge through partials touch memory beyond o and lse
+    workspace = nullptr;
+    if (nsplit > fattn::kDecodeWgMaxSplits) {
+      if (fattn::decode_scratch(&workspace) != hipSuccess) return FATTN_EHIP;
+    }
+  } else if (!workspace || workspace_bytes < need || !aligned16(workspace)) {
+    return FATTN_EWORKSPACE;
+  }
 
   size_t rows = size_t(B) * size_t(Hq) * size_t(nsplit);
   size_t o_bytes = (rows * size_t(d) * sizeof(float) + 255) / 256 * 256;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes)
+                              : nullptr;
   fattn::DecodeArgs a{q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale,
-                      nsplit, chunk, static_cast<float*>(workspace),
-                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes), bits,
-                      seqlens};
+                      nsplit, chunk, part_o, part_lse, bits, seqlens};
   hipError_t err = fattn::launch_decode(a, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? FATTN_OK : FATTN_EHIP;
 }
@@ -264,6 +278,14 @@ int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_scale,
                       void* stream) {
   return decode(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits,
                 workspace, workspace_bytes, stream, 8);
+}
+
+int fattn_decode_int8_noalloc(const void* q, const int8_t* kq, const float* k_scale,
+                              const int8_t* vq, const float* v_scale, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Skv, int d, float scale,
+                              int num_splits, void* stream) {
+  return decode(q, kq, k_scale, vq, v_scale, o, lse, B, Hq, Hkv, Skv, d, scale, num_splits,
+                kBuiltinScratch, 0, stream, 8);
 }
 
 int fattn_decode_int4(const void* q, const uint8_t* kq, const float* k_scale,

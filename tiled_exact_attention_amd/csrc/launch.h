@@ -91,6 +91,19 @@ hipError_t launch_kv_quant(const KvQuantArgs& a, hipStream_t stream);
 // Key-tile length of the decode split kernel; split chunks are multiples of it.
 constexpr int kDecodeTile = 64;
 
+// Most splits per (b, kv head) stream that one workgroup holds and merges on
+// chip; plans with more splits merge through the workspace partials.
+constexpr int kDecodeWgMaxSplits = 8;
+
+// Size of the decode's built-in scratch array (one per GPU, allocated when the
+// library's code object is loaded on that GPU and held until the process
+// ends), used instead of a caller workspace by fattn_decode_int8_noalloc.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+
+// Device address of the built-in scratch array on the current device
+// (hipGetSymbolAddress, taken once per device and kept).
+hipError_t decode_scratch(void** ptr);
+
 // Enqueues kernel<<<grid, block, lds, stream>>>(args...) and returns the
 // status of that launch itself (hipLaunchKernel's result), never an error
 // left pending by an earlier HIP call: the library does not call
