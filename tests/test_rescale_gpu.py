@@ -160,7 +160,9 @@ def test_bwd_with_climbing_scores(case, cuda_device):
     # (2^-9 relative) sets the error of dQ and dK rather than the products'.
     # The oracle therefore forms D from its own forward output rounded to bf16
     # (RNE), as stored; bounds as for every gradient (2^-6 of the max, 2^-7 of
-    # the rms, relative to each gradient's own scale).
+    # the rms, relative to each gradient's own scale).  The distance to the
+    # true gradient is then measured and printed as well, dq bounded by the
+    # shift the stored output's rounding explains.
     B, Hq, Hkv, Sq, Skv, d, causal, window, profile = case
     _say(f"case rescale bwd {case}")
     scale = 1 / math.sqrt(d)
@@ -188,3 +190,25 @@ def test_bwd_with_climbing_scores(case, cuda_device):
         assert err.max() <= GRAD_MAX_REL * mx + GRAD_MAX_ABS, f"{name}: max {err.max():.3e} (ref {mx:.3e})"
         assert err.mean() <= GRAD_MEAN_REL * rms + GRAD_MEAN_ABS, f"{name}: mean {err.mean():.3e} (rms {rms:.3e})"
     _say("  rel max/mean: " + " ".join(msg))
+
+    # Against the true gradient (D from the exact output): dv does not use D;
+    # dq moves by exactly scale * (D_stored - D_true)_i * (P K)_i per row, and
+    # RNE to bf16 bounds |D_stored - D_true|_i by 2^-9 * sum_c |dO_ic O_ic|, so
+    # |dq - dq_true| <= the bar above + scale * 2^-9 * sum_c |dO O| * |P K|,
+    # with P K the forward with V := K.  dk is reported: its shift sums the
+    # same row terms over the queries that see each key.
+    true = oracle.bwd(q, k, v, do, causal=causal, window=window, scale=scale)
+    pk, _ = oracle.fwd(q, k, k, causal=causal, window=window, scale=scale)
+    d_bound = 2.0 ** -9 * np.sum(np.abs(do.double().numpy()) * np.abs(o_ref), axis=-1, keepdims=True)
+    shift = abs(scale) * d_bound * np.abs(pk)
+    msg = []
+    for name, a, r in (("dq", dq, true[0]), ("dk", dk, true[1]), ("dv", dv, true[2])):
+        err = np.abs(_np64(a) - r)
+        msg.append(f"{name} {err.max():.3e} (of max |grad| {np.abs(r).max():.3e})")
+        if name == "dq":
+            bar = GRAD_MAX_REL * np.abs(r).max() + GRAD_MAX_ABS
+            assert np.all(err <= bar + shift), f"dq vs the true gradient: {err.max():.3e}"
+        if name == "dv":
+            assert err.max() <= GRAD_MAX_REL * np.abs(r).max() + GRAD_MAX_ABS
+    _say(f"  max-abs against the true gradient (D from the exact output): " + ", ".join(msg) +
+         f"; stored-output shift bound on dq {shift.max():.3e}")
