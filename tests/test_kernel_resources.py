@@ -4,7 +4,7 @@ The kernels are designed around a number of waves per SIMD (the prefill
 pipelines two waves per SIMD at d = 128 and three at d = 64; the dK/dV
 backward kernel runs one), and none may spill to scratch memory.  A change
 that adds a few registers can silently drop a kernel to fewer resident waves
-(the d = 64 prefill kernel sits at 166 of the 168 registers that three waves
+(the d = 64 prefill kernel uses 149 of the 168 registers that three waves
 allow), so this compiles each HIP source's device code to gfx950 assembly and
 checks the per-kernel figures hipcc writes there.  CPU only (hipcc
 cross-compiles).

@@ -212,28 +212,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   const int64_t kv_stride = int64_t(p.Hkv) * D;
   const __bf16* kbase = p.k + (sv.k_row0 * p.Hkv + hk) * D;
   const __bf16* vbase = p.v + (sv.k_row0 * p.Hkv + hk) * D;
-  // element offset of this lane's source chunk within a tile (|offset| <
-  // 64 rows of Hkv * d elements, checked on the host to fit 32 bits)
-  int goff[NLD];
+  // byte offset of this lane's source chunk from the first row of a tile
+  // (non-negative and below 2^31: 64 rows of Hkv * d elements, checked on
+  // the host), so every copy addresses a scalar base plus a 32-bit lane
+  // offset and no lane holds a 64-bit address (measured on MI355X: 28 fewer
+  // registers at d = 128, bit-identical, 1-2% faster at d = 128)
+  uint32_t goff[NLD];
   const int lr = lane / KCH;
+  const uint32_t row_b = uint32_t(kv_stride) * 2u;  // bytes per key row
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int r = 16 * w + LPI * i + lane / KCH;
-    goff[i] = r * int(kv_stride) + ((lane % KCH) ^ swz<D>(r)) * 8;
+    const int r = 16 * w + LPI * i + lr;
+    goff[i] = uint32_t(r) * row_b + uint32_t(((lane % KCH) ^ swz<D>(r)) * 16);
   }
   // copy rows j0 .. j0+63 of one tensor (K or V) into an LDS buffer; on the
   // last tile of the sequence, rows past the end re-read the last row
   auto issue_tile = [&](const __bf16* base, int64_t j0, char* dst_tile) __attribute__((always_inline)) {
+    const char* src = reinterpret_cast<const char*>(base + j0 * kv_stride);
     if (j0 + kBN <= Skv) {
-      const __bf16* src = base + j0 * kv_stride;
 #pragma unroll
       for (int i = 0; i < NLD; ++i) global_to_lds16(src + goff[i], dst_tile + (16 * w + LPI * i) * ROWB);
     } else {
+      const int last = int(Skv - 1 - j0);  // last row of the sequence within this tile
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int row = 16 * w + LPI * i + lr;
-        const int64_t j = min(j0 + row, int64_t(Skv) - 1);
-        global_to_lds16(base + goff[i] + (j - row) * kv_stride, dst_tile + (16 * w + LPI * i) * ROWB);
+        const int r = 16 * w + LPI * i + lr;
+        const uint32_t back = uint32_t(max(r - last, 0)) * row_b;
+        global_to_lds16(src + (goff[i] - back), dst_tile + (16 * w + LPI * i) * ROWB);
       }
     }
   };
