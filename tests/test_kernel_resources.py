@@ -24,15 +24,23 @@ MIN_OCCUPANCY = {
     "fwd_bf16_kernel<128>": 2,
     "fwd_f32_kernel<64>": 2,
     "fwd_f32_kernel<128>": 1,
-    # <D, code bits, workgroup form>
-    "decode_split_kernel<64,8,0>": 3,
-    "decode_split_kernel<64,4,0>": 4,
-    "decode_split_kernel<128,8,0>": 2,
-    "decode_split_kernel<128,4,0>": 2,
-    "decode_split_kernel<64,8,1>": 3,
-    "decode_split_kernel<64,4,1>": 4,
-    "decode_split_kernel<128,8,1>": 2,
-    "decode_split_kernel<128,4,1>": 2,
+    # <D, code bits, workgroup form, non-temporal loads>
+    "decode_split_kernel<64,8,0,0>": 3,
+    "decode_split_kernel<64,8,0,1>": 3,
+    "decode_split_kernel<64,8,1,0>": 3,
+    "decode_split_kernel<64,8,1,1>": 3,
+    "decode_split_kernel<64,4,0,0>": 4,
+    "decode_split_kernel<64,4,0,1>": 4,
+    "decode_split_kernel<64,4,1,0>": 4,
+    "decode_split_kernel<64,4,1,1>": 4,
+    "decode_split_kernel<128,8,0,0>": 2,
+    "decode_split_kernel<128,8,0,1>": 2,
+    "decode_split_kernel<128,8,1,0>": 2,
+    "decode_split_kernel<128,8,1,1>": 2,
+    "decode_split_kernel<128,4,0,0>": 2,
+    "decode_split_kernel<128,4,0,1>": 2,
+    "decode_split_kernel<128,4,1,0>": 2,
+    "decode_split_kernel<128,4,1,1>": 2,
     "decode_merge_kernel<64>": 8,
     "decode_merge_kernel<128>": 8,
     "bwd_pre_kernel<64>": 8,
