@@ -11,7 +11,10 @@ call's cache lines in the last-level cache).  `value` is the prefill
 attention throughput in TFLOP/s (4*d FLOPs per visible (query, key) pair per
 query head, counted exactly); the decode leg reports HBM GB/s over its
 algorithmic bytes (int8 K and V, their fp32 scales, the bf16 query and output).
-Each timed step runs the prefill launch, then the decode call; HIP events
+Before the W warmup steps the step runs untimed for --settle-ms of wall time
+(default 200 ms): the chip raises its clocks over the first tens of
+milliseconds of load.  Each timed step runs the prefill launch, then the
+decode call; HIP events
 recorded on the launch stream (torch's current stream, which the binding
 passes to libfattn) at the step and leg boundaries time each call.  The
 sustained rate of K prefill launches in a row is reported beside it
@@ -187,6 +190,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--num-splits", type=int, default=0, help="decode key splits (0 = library default)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="wall time of untimed steps before the warmup steps, while the chip's clocks rise")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -287,6 +292,24 @@ def main():
         if st != 0:
             raise fa.FattnError(st, "fattn_decode_int8")
 
+    # Clock settle: the chip raises its clocks over the first tens of
+    # milliseconds of load (measured on MI355X: prefill launches of the step
+    # take 401, 334, 304, 292 and then about 286 us per group of 10 steps
+    # after process start, idle before or not), so the step runs untimed for
+    # a fixed wall time before the warmup steps; the timed region is unchanged.
+    settle_steps = 0
+    if args.settle_ms > 0:
+        log(f"settle: steps for {args.settle_ms:.0f} ms (untimed)")
+        t_end = time.perf_counter() + args.settle_ms / 1e3
+        while time.perf_counter() < t_end:
+            for _ in range(5):
+                if do_prefill:
+                    run_prefill()
+                if do_decode:
+                    run_decode(settle_steps)
+                settle_steps += 1
+            torch.cuda.synchronize()
+
     log(f"warmup {args.warmup} steps")
     for s in range(args.warmup):
         if do_prefill:
@@ -344,6 +367,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "settle": {"ms": args.settle_ms, "steps": settle_steps,
+                   "note": "untimed steps before the warmup steps while the chip's clocks rise under load"},
         "config": {"workload": f"{wp.name} + {wd.name}", "prefill": {
             "B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "S": wp.Sq, "d": wp.d, "causal": wp.causal,
             "layout": "BSHD", "seed": wp.seed}, "decode": {

@@ -275,13 +275,13 @@ def report(indir, outdir=PROFILES):
     with open(os.path.join(outdir, "kernels_bench_run.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    # headline summaries.  The benchmark runs W warmup steps and then its K
-    # timed steps (prefill launch, decode call) before anything else; later
-    # legs reuse the same kernels and grids (back-to-back prefills, the
-    # backward's forward, the varlen decode), so the timed steps' dispatches
-    # are the W+1-th to the W+K-th of each kernel.
+    # headline summaries.  The benchmark runs its settle steps, W warmup
+    # steps and then its K timed steps (prefill launch, decode call) before
+    # anything else; later legs reuse the same kernels and grids (back-to-back
+    # prefills, the backward's forward, the varlen decode), so the timed
+    # steps' dispatches are the K that follow the settle and warmup steps.
     bench = passes["trace"]["bench"] or {}
-    w0 = int(bench.get("warmup", 0))
+    w0 = int((bench.get("settle") or {}).get("steps", 0)) + int(bench.get("warmup", 0))
     timed = slice(w0, w0 + int(bench.get("steps", 0))) if bench.get("steps") else slice(None)
     pdur = _match(trace, PREFILL_KERNEL, PREFILL_GRID)[timed]
     pavg = statistics.mean(pdur)

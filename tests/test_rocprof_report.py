@@ -54,13 +54,13 @@ def _counter_rows(i, name, grid, counters):
 @pytest.fixture
 def collected(tmp_path):
     d = tmp_path / "prof"
-    steps, warmup = 3, 1
-    # trace: one warmup step (500 us, 700 us: not timed), the timed steps (300 us
-    # prefill, 400 us decode), then later legs with the same kernels and grids
-    # that must not count (900 / 100 us)
+    steps, warmup, settle = 3, 1, 2
+    # trace: two settle steps and one warmup step (500 us, 700 us: not timed),
+    # the timed steps (300 us prefill, 400 us decode), then later legs with the
+    # same kernels and grids that must not count (900 / 100 us)
     rows, t, i = [], 10 ** 9, 0
-    for s in range(warmup + steps):
-        dp, dd = (500.0, 700.0) if s < warmup else (300.0, 400.0)
+    for s in range(settle + warmup + steps):
+        dp, dd = (500.0, 700.0) if s < settle + warmup else (300.0, 400.0)
         rows.append(_trace_row(i, PREFILL, R.PREFILL_GRID, t, dp, 256)); i += 1; t += 10 ** 6
         rows.append(_trace_row(i, DECODE, R.DECODE_GRID, t, dd, 512)); i += 1; t += 10 ** 6
     rows.append(_trace_row(i, PREFILL, R.PREFILL_GRID, t, 900.0, 256)); i += 1; t += 10 ** 6
@@ -87,7 +87,7 @@ def collected(tmp_path):
             for j in (1, 2, 3):
                 rows += _counter_rows(j, name, grid, {cname: val})
             _write(str(d / f"{kind}_{leg}" / "run_counter_collection.csv"), COUNTER_COLS, rows)
-    bench_line = {"steps": steps, "warmup": warmup,
+    bench_line = {"steps": steps, "warmup": warmup, "settle": {"ms": 200.0, "steps": settle},
                   "roofline": {"avg_launch_us": 301.0, "achieved": 913.0},
                   "decode": {"avg_call_us": 401.0, "value": 5524.0}}
     passes = {name: {"cmd": f"rocprofv3 ... {name}", "returncode": 0,
@@ -121,7 +121,7 @@ def test_report_reduces_traces_and_counters(collected, tmp_path):
     gbs = decode_bytes(W.INT8_DECODE) / 400e-6 / 1e9
     assert "| 3 | 400.0 | 400.0 | 400.0 |" in dec and f"{gbs:.1f}" in dec
     table = open(os.path.join(out, "kernels_bench_run.md")).read()
-    assert "| `fwd_bf16_kernel<128>` | 524288 | 5 |" in table  # every dispatch in the overall table
+    assert "| `fwd_bf16_kernel<128>` | 524288 | 7 |" in table  # every dispatch in the overall table
     assert "| 50.0% | 280.000 |" in table
 
 
