@@ -48,6 +48,13 @@ __device__ __forceinline__ void store_nt16(void* p, const uint4& v) {
 __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
 }
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt8(void* p, uint32_t lo, uint32_t hi) {
+  __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void store_nt4(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -23,6 +23,10 @@
 // 16-byte loads in flight.  The row's absmax is reduced with cross-lane xor
 // shuffles; each lane stores its 8 codes as one 8-byte (int8) or 4-byte
 // (int4) write into the head-major cache, the row's first lane the scale.
+// The input rows and the codes carry the non-temporal hint (each byte is
+// touched once); measured on MI355X for B32 T32768 Hkv8 d128 bf16 rows:
+// int8 625 -> 604 us, int4 523 -> 510 us (the hint on the loads alone was
+// slower, on the stores alone equal).
 #include <type_traits>
 
 #include "device_util.h"
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void kv_quant_kernel(const T* __restrict_
     const int64_t r = r0 + int64_t(i) * RPP;
     const T* src = x + (r < rows ? r : 0) * D + 8 * lane_in_row;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) raw[i][j] = reinterpret_cast<const Raw*>(src)[j];
+    for (int j = 0; j < kLoads; ++j) raw[i][j] = __builtin_bit_cast(Raw, load_nt16(reinterpret_cast<const Raw*>(src) + j));
   }
 
 #pragma unroll
@@ -112,9 +116,9 @@ __global__ __launch_bounds__(kThreads) void kv_quant_kernel(const T* __restrict_
       const I t = bt - b * I(Tn);
       const int64_t slot = (int64_t(b) * Hkv + int64_t(h)) * int64_t(cap) + pos + int64_t(t);
       if constexpr (BITS == 8) {
-        *reinterpret_cast<uint2*>(codes + slot * RB + 8 * lane_in_row) = make_uint2(lo, hi);
+        store_nt8(codes + slot * RB + 8 * lane_in_row, lo, hi);
       } else {
-        *reinterpret_cast<uint32_t*>(codes + slot * RB + 4 * lane_in_row) = lo;
+        store_nt4(codes + slot * RB + 4 * lane_in_row, lo);
       }
       if (lane_in_row == 0) scales[slot] = scale;
     }
