@@ -240,6 +240,12 @@ def main():
                           dtype=torch.uint8, device=dev)
         bout = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         call = lambda: fa.bwd(q, k, v, o, lse, bdo, causal=wp.causal, scale=wp.scale, workspace=bws, out=bout)
+        settle_calls = 0
+        t_end = time.perf_counter() + args.settle_ms / 1e3  # untimed, while the clocks rise
+        while time.perf_counter() < t_end:
+            call()
+            torch.cuda.synchronize()
+            settle_calls += 1
         for _ in range(args.warmup):
             call()
         torch.cuda.synchronize()
@@ -252,7 +258,9 @@ def main():
         us = e0.elapsed_time(e1) * 1e3 / max(args.steps, 1)
         bflops = 2.5 * prefill_flops(wp)
         print(json.dumps({"workload": f"backward of {wp.name}", "avg_us": round(us, 2),
-                          "TFLOP/s": round(bflops / (us * 1e-6) / 1e12, 2)}), flush=True)
+                          "TFLOP/s": round(bflops / (us * 1e-6) / 1e12, 2), "steps": args.steps,
+                          "warmup": args.warmup, "settle": {"ms": args.settle_ms, "steps": settle_calls}}),
+              flush=True)
         return
     do_prefill = args.only in ("all", "prefill")
     do_decode = args.only in ("all", "decode")
@@ -407,8 +415,9 @@ def main():
                             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                                          "traffic": read_traffic(DECODE_KERNEL_SRC, "decode"),
-                                         "kernel": "decode_split_kernel<128, 8, true> (8 splits per "
-                                                   "stream merged in the workgroup: one launch)",
+                                         "kernel": "decode_split_kernel<128, 8, true, true> (8 splits per "
+                                                   "stream merged in the workgroup: one launch; "
+                                                   "non-temporal cache loads)",
                                          "algorithmic_bytes_per_call": nbytes}}
         if not do_prefill:
             result["value"], result["unit"] = round(gbs, 1), "GB/s"

@@ -5,9 +5,10 @@ of the benchmark on an MI355X and reduces them to the summaries in profiles/.
     python rocprof_report.py report DIR    # reads DIR's CSVs, rewrites profiles/
 
 ``collect`` runs one rocprofv3 process per pass (kernel trace, matrix-core
-counters, then HBM read and write counters of a plain 1 GiB copy, of the
-prefill leg and of the decode leg), each as a child process under its own
-time limit, and writes DIR/manifest.json with the exact commands, the
+counters, HBM read and write counters of a plain 1 GiB copy, of the prefill
+leg and of the decode leg, LDS / stall / instruction counters of the
+prefill leg, then a kernel trace and the same counters of the backward),
+each as a child process under its own time limit, and writes DIR/manifest.json with the exact commands, the
 bench's JSON line of each pass and the hash of every kernel source.
 
 ``report`` reduces what collect left:
@@ -23,7 +24,10 @@ bench's JSON line of each pass and the hash of every kernel source.
 It writes profiles/kernels_bench_run.md, profiles/hbm_traffic.txt (read by
 bench.py for roofline.traffic, keyed by kernel-source hash) and the two
 headline summaries profiles/fwd_bf16_mha_causal_b2_h32_s4096_d128.md and
-profiles/decode_int8_b32_hq32_hkv8_skv32768_d128.md.
+profiles/decode_int8_b32_hq32_hkv8_skv32768_d128.md, the prefill kernel's LDS,
+stall and overlap counters (profiles/fwd_bf16_counters_mha_causal_b2_h32_s4096_d128.md)
+and the backward's kernel trace, counters and HBM traffic
+(profiles/bwd_mha_causal_b2_h32_s4096_d128.md).
 """
 from __future__ import annotations
 
@@ -49,16 +53,33 @@ COPY_BYTES = 1 << 30  # bench.py --only copy: one 1 GiB device-to-device copy pe
 
 # (pass name, rocprofv3 options, bench.py arguments).  Counter passes stay
 # within one hardware pass (FETCH_SIZE uses 3 TCC counters, WRITE_SIZE 2).
-BENCH_SHORT = ["--steps", "2", "--warmup", "1", "--no-cpu-baseline"]
+# Counter passes skip the bench's clock-settle phase (the counters are
+# ratios per dispatch; under the profiler every dispatch is serialised).
+BENCH_SHORT = ["--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--settle-ms", "0"]
+BWD_SHORT = ["--only", "bwd", "--steps", "2", "--warmup", "1", "--settle-ms", "0"]
+PREFILL_SHORT = ["--only", "prefill"] + BENCH_SHORT
+# SQ counters for the stall / overlap tables (at most 8 SQ and 2 GRBM per pass)
+LDS_COUNTERS = ["SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_ADDR_CONFLICT", "SQ_WAIT_INST_LDS",
+                "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE"]
+INST_COUNTERS = ["SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE"]
 PASSES = [
     ("trace", ["--kernel-trace", "--stats"], ["--steps", "10", "--warmup", "2", "--no-cpu-baseline"]),
     ("mfma", ["--pmc", "MfmaUtil", "MfmaFlopsBF16", "GRBM_GUI_ACTIVE"], BENCH_SHORT),
     ("fetch_copy", ["--pmc", "FETCH_SIZE"], ["--only", "copy", "--steps", "2", "--warmup", "1"]),
     ("write_copy", ["--pmc", "WRITE_SIZE"], ["--only", "copy", "--steps", "2", "--warmup", "1"]),
-    ("fetch_prefill", ["--pmc", "FETCH_SIZE"], ["--only", "prefill"] + BENCH_SHORT),
-    ("write_prefill", ["--pmc", "WRITE_SIZE"], ["--only", "prefill"] + BENCH_SHORT),
+    ("fetch_prefill", ["--pmc", "FETCH_SIZE"], PREFILL_SHORT),
+    ("write_prefill", ["--pmc", "WRITE_SIZE"], PREFILL_SHORT),
     ("fetch_decode", ["--pmc", "FETCH_SIZE"], ["--only", "decode"] + BENCH_SHORT),
     ("write_decode", ["--pmc", "WRITE_SIZE"], ["--only", "decode"] + BENCH_SHORT),
+    ("lds_prefill", ["--pmc"] + LDS_COUNTERS, PREFILL_SHORT),
+    ("inst_prefill", ["--pmc"] + INST_COUNTERS, PREFILL_SHORT),
+    ("bwd_trace", ["--kernel-trace", "--stats"], ["--only", "bwd", "--steps", "5", "--warmup", "2"]),
+    ("bwd_mfma", ["--pmc", "MfmaUtil", "MfmaFlopsBF16", "GRBM_GUI_ACTIVE"], BWD_SHORT),
+    ("lds_bwd", ["--pmc"] + LDS_COUNTERS, BWD_SHORT),
+    ("inst_bwd", ["--pmc"] + INST_COUNTERS, BWD_SHORT),
+    ("fetch_bwd", ["--pmc", "FETCH_SIZE"], BWD_SHORT),
+    ("write_bwd", ["--pmc", "WRITE_SIZE"], BWD_SHORT),
 ]
 
 # The benchmark's headline kernels: the MHA causal prefill (B2 H32 S4096
@@ -66,7 +87,7 @@ PASSES = [
 # Skv32768 d128: one 512-thread workgroup per (batch, kv head)).
 PREFILL_KERNEL = re.compile(r"fwd_bf16_kernel<128>")
 PREFILL_GRID = 2048 * 256
-DECODE_KERNEL = re.compile(r"decode_split_kernel<128, ?8")
+DECODE_KERNEL = re.compile(r"decode_split_kernel<128, ?8, ?true, ?true>")  # varlen: <..., false>, same grid
 DECODE_GRID = 32 * 8 * 512
 LIBRARY_KERNEL = re.compile(r"(fwd_bf16|fwd_f32|decode_split|decode_merge|bwd_\w+|kv_quant)_kernel")
 
@@ -220,6 +241,61 @@ def algorithmic():
     return prefill_flops(wp), qkvo, decode_bytes(wd)
 
 
+def stall_rows(lds, inst, mfma, kernel_re):
+    """Per (kernel, grid) matching kernel_re: medians over dispatches of the
+    LDS, wait and instruction counters, as fractions.  GRBM_GUI_ACTIVE is
+    summed over the 8 XCDs, so one XCD's active cycles are an eighth of it:
+    CU-cycles = that x 256 CUs, SIMD-cycles = that x 1024 SIMDs.  The wave
+    counters and SQ_ACTIVE_INST_VALU count quad-cycles."""
+    rows = []
+    for key in sorted(set(lds) | set(inst)):
+        if not kernel_re.search(key[0]):
+            continue
+        m = lambda d, c: statistics.median(d[key][c]) if key in d and d[key].get(c) else None
+        g_l, g_i = m(lds, "GRBM_GUI_ACTIVE"), m(inst, "GRBM_GUI_ACTIVE")
+        cu = g_l / 8 * 256 if g_l else None
+        simd = g_i / 8 * 1024 if g_i else None
+        r = {"kernel": key[0], "grid": key[1]}
+        if cu:
+            r["lds_busy"] = m(lds, "SQ_LDS_IDX_ACTIVE") / cu
+            r["bank_conflict"] = m(lds, "SQ_LDS_BANK_CONFLICT") / cu
+            r["addr_conflict"] = m(lds, "SQ_LDS_ADDR_CONFLICT") / cu
+            wc = m(lds, "SQ_WAVE_CYCLES")
+            r["waves_per_cu"] = 4 * wc / cu
+            r["wait_any"] = m(lds, "SQ_WAIT_ANY") / wc
+            r["wait_lds"] = m(lds, "SQ_WAIT_INST_LDS") / wc
+        if simd:
+            r["mfma_busy"] = m(inst, "SQ_VALU_MFMA_BUSY_CYCLES") / simd
+            r["valu_active"] = 4 * m(inst, "SQ_ACTIVE_INST_VALU") / simd
+            nm = m(inst, "SQ_INSTS_MFMA")
+            r["valu_per_mfma"] = (m(inst, "SQ_INSTS_VALU") - nm) / nm if nm else None
+            r["lds_per_mfma"] = m(inst, "SQ_INSTS_LDS") / nm if nm else None
+        mu = m(mfma, "MfmaUtil")
+        r["mfma_util"] = mu / 100 if mu is not None else None
+        rows.append(r)
+    return rows
+
+
+def _pct(x, digits=1):
+    return "-" if x is None else f"{100 * x:.{digits}f}%"
+
+
+def stall_table(rows):
+    out = ["| kernel | MfmaUtil | matrix busy | VALU active | busy sum | LDS busy | bank conflicts "
+           "| waves per CU | waves waiting | waiting to issue LDS | VALU / LDS instr per product |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        busy = (r["mfma_busy"] + r["valu_active"]) if "mfma_busy" in r else None
+        ratio = (f"{r['valu_per_mfma']:.2f} / {r['lds_per_mfma']:.2f}"
+                 if r.get("valu_per_mfma") is not None else "-")
+        waves = f"{r['waves_per_cu']:.1f}" if "waves_per_cu" in r else "-"
+        out.append(f"| `{r['kernel']}` | {_pct(r.get('mfma_util'))} | {_pct(r.get('mfma_busy'))} | "
+                   f"{_pct(r.get('valu_active'))} | {_pct(busy)} | {_pct(r.get('lds_busy'))} | "
+                   f"{_pct(r.get('bank_conflict'), 2)} | {waves} | {_pct(r.get('wait_any'))} | "
+                   f"{_pct(r.get('wait_lds'))} | {ratio} |")
+    return out
+
+
 def report(indir, outdir=PROFILES):
     with open(os.path.join(indir, "manifest.json")) as f:
         man = json.load(f)
@@ -252,7 +328,8 @@ def report(indir, outdir=PROFILES):
         f.write(f"prefill_fetch_kib_raw: {traffic['prefill'][0]:.1f}\nprefill_write_kib_raw: {traffic['prefill'][1]:.1f}\n")
         f.write(f"prefill_hbm_bytes_per_launch: {traffic['prefill'][2]:.0f}\n")
         f.write(f"prefill_source_sha256: {src['fwd_bf16.hip']}\n")
-        f.write("decode_kernels: decode_split_kernel<128, 8, true> (B32 Hq32 Hkv8 Skv32768 d128, merged in the workgroup)\n")
+        f.write("decode_kernels: decode_split_kernel<128, 8, true, true> (B32 Hq32 Hkv8 Skv32768 d128, merged in the "
+                "workgroup, non-temporal cache loads)\n")
         f.write(f"decode_fetch_kib_raw: {traffic['decode'][0]:.1f}\ndecode_write_kib_raw: {traffic['decode'][1]:.1f}\n")
         f.write(f"decode_hbm_bytes_per_launch: {traffic['decode'][2]:.0f}\n")
         f.write(f"decode_source_sha256: {src['decode_kv.hip']}\n")
@@ -315,14 +392,14 @@ def report(indir, outdir=PROFILES):
     dgbs = decode_alg_bytes / (davg * 1e-6) / 1e9
     fk, wk, tot = traffic["decode"]
     with open(os.path.join(outdir, "decode_int8_b32_hq32_hkv8_skv32768_d128.md"), "w") as f:
-        f.write("# decode_split_kernel<128, 8, true>: int8-cache decode, B=32, Hq=32, Hkv=8, Skv=32768, d=128\n\n"
+        f.write("# decode_split_kernel<128, 8, true, true>: int8-cache decode, B=32, Hq=32, Hkv=8, Skv=32768, d=128\n\n"
                 "One launch per call: the 8 splits of each (batch, kv head) stream are the waves of one "
                 "workgroup and are merged in LDS.  Written by `python rocprof_report.py report <dir>`.  "
                 "Kernel trace (repo root):\n\n"
                 f"    {passes['trace']['cmd']}\n\n"
                 "| kernel | dispatches | avg us | min us | max us | GB/s at avg | of 8 TB/s |\n"
                 "|---|---|---|---|---|---|---|\n"
-                f"| `decode_split_kernel<128, 8, true>` (the bench's timed steps) | {len(ddur)} | {davg:.1f} | {min(ddur):.1f} | "
+                f"| `decode_split_kernel<128, 8, true, true>` (the bench's timed steps) | {len(ddur)} | {davg:.1f} | {min(ddur):.1f} | "
                 f"{max(ddur):.1f} | {dgbs:.1f} | {dgbs / PEAK_HBM_GBS:.1%} |\n\n"
                 f"Algorithmic bytes: {decode_alg_bytes} per call (int8 K and V, fp32 scales, bf16 q and o).\n")
         dec = bench.get("decode", {})
@@ -332,6 +409,75 @@ def report(indir, outdir=PROFILES):
         f.write(f"\nHBM traffic (copy-scaled FETCH_SIZE {fk:.1f} KiB and WRITE_SIZE {wk:.1f} KiB): "
                 f"{tot / 1e6:.1f} MB per call against {decode_alg_bytes / 1e6:.1f} MB algorithmic "
                 f"({tot / decode_alg_bytes:.3f}x).\n")
+    # LDS, stall and overlap counters of the prefill kernel(s)
+    lds_p = counters(os.path.join(indir, "lds_prefill"))
+    inst_p = counters(os.path.join(indir, "inst_prefill"))
+    rows = stall_rows(lds_p, inst_p, mf, re.compile(r"fwd_bf16_kernel"))
+    with open(os.path.join(outdir, "fwd_bf16_counters_mha_causal_b2_h32_s4096_d128.md"), "w") as f:
+        f.write("# fwd_bf16_kernel: LDS, wave stalls and matrix / vector overlap, MI355X\n\n"
+                "Written by `python rocprof_report.py report <dir>` from three counter passes of the "
+                "prefill leg and the bench run's matrix-core pass (repo root):\n\n")
+        for name in ("lds_prefill", "inst_prefill", "mfma"):
+            f.write(f"    {passes[name]['cmd']}\n")
+        f.write(f"\nMedians over dispatches; rows are (kernel, grid size in work-items), the MHA causal "
+                f"B2 H32 S4096 d128 launch is grid {PREFILL_GRID}.  GRBM_GUI_ACTIVE is summed over the 8 XCDs, "
+                "so one XCD's active cycles are an eighth of it: CU-cycles = that x 256, SIMD-cycles = that x "
+                "1024.  Matrix busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD-cycles (the same ratio as MfmaUtil, "
+                "from another pass); VALU active = 4 x SQ_ACTIVE_INST_VALU (quad-cycles) / SIMD-cycles; "
+                "LDS busy and bank conflicts per CU-cycle; waves waiting and waiting to issue an LDS "
+                "instruction per wave-cycle (SQ_WAIT_ANY, SQ_WAIT_INST_LDS over SQ_WAVE_CYCLES); VALU "
+                "(non-matrix) and LDS instructions per matrix product from SQ_INSTS_*.  A busy sum near 100% "
+                "means the matrix and vector work of a SIMD hardly overlap.\n\n")
+        f.write("\n".join(stall_table(rows)) + "\n")
+        f.write("\n| kernel | grid |\n|---|---|\n" + "".join(f"| `{r['kernel']}` | {r['grid']} |\n" for r in rows))
+
+    # the backward of the MHA workload
+    btrace = kernel_trace(os.path.join(indir, "bwd_trace"))
+    bmf = counters(os.path.join(indir, "bwd_mfma"))
+    brows = stall_rows(counters(os.path.join(indir, "lds_bwd")), counters(os.path.join(indir, "inst_bwd")),
+                       bmf, re.compile(r"bwd_\w+_kernel"))
+    bfe = counters(os.path.join(indir, "fetch_bwd"))
+    bwr = counters(os.path.join(indir, "write_bwd"))
+    bb = passes["bwd_trace"]["bench"] or {}
+    b0 = int((bb.get("settle") or {}).get("steps", 0)) + int(bb.get("warmup", 0))
+    bsl = slice(b0, b0 + int(bb.get("steps", 0))) if bb.get("steps") else slice(None)
+    bflops = 2.5 * flops
+    with open(os.path.join(outdir, "bwd_mha_causal_b2_h32_s4096_d128.md"), "w") as f:
+        f.write("# Backward of the MHA causal prefill (B2 H32 S4096 d128, bf16), MI355X\n\n"
+                "Written by `python rocprof_report.py report <dir>`.  Kernel trace (repo root; the "
+                "backward alone after an untimed clock-settle phase, durations of the timed calls):\n\n"
+                f"    {passes['bwd_trace']['cmd']}\n\n"
+                "| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|\n")
+        tot = 0.0
+        for (k, g), durs in sorted(btrace.items(), key=lambda kv: -sum(kv[1])):
+            if not k.startswith("bwd_"):
+                continue
+            d = durs[bsl] or durs
+            tot += statistics.mean(d)
+            f.write(f"| `{k}` | {len(d)} | {statistics.mean(d):.1f} | {min(d):.1f} | {max(d):.1f} |\n")
+        f.write(f"\nSum of the kernels' averages: {tot:.1f} us per backward, {bflops / (tot * 1e-6) / 1e12:.1f} "
+                f"TFLOP/s at 2.5x the forward's algorithmic FLOPs ({bflops / (tot * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.1%} "
+                "of 2.5 PFLOP/s).")
+        if bb.get("avg_us"):
+            f.write(f"  The bench line of the same run (HIP events around the timed calls): {bb['avg_us']} us "
+                    f"per call, {bb.get('TFLOP/s')} TFLOP/s.")
+        f.write("\n\nCounters (repo root, one pass each):\n\n")
+        for name in ("bwd_mfma", "lds_bwd", "inst_bwd", "fetch_bwd", "write_bwd"):
+            f.write(f"    {passes[name]['cmd']}\n")
+        f.write("\nRatios as in `fwd_bf16_counters_mha_causal_b2_h32_s4096_d128.md`:\n\n")
+        f.write("\n".join(stall_table(brows)) + "\n\n")
+        f.write("HBM traffic per dispatch (copy-scaled FETCH_SIZE and WRITE_SIZE):\n\n"
+                "| kernel | read MB | written MB |\n|---|---|---|\n")
+        for key in sorted(set(bfe) | set(bwr)):
+            if not key[0].startswith("bwd_"):
+                continue
+            rd = statistics.median(bfe[key]["FETCH_SIZE"]) * 1024 * fetch_scale / 1e6 if key in bfe else float("nan")
+            wr = statistics.median(bwr[key]["WRITE_SIZE"]) * 1024 * write_scale / 1e6 if key in bwr else float("nan")
+            f.write(f"| `{key[0]}` | {rd:.1f} | {wr:.1f} |\n")
+        qkvo = prefill_alg_bytes
+        f.write(f"\nAlgorithmic bytes of the backward: q, k, v, o, dO read and dq, dk, dv written, "
+                f"{2 * qkvo / 1e6:.1f} MB (plus the fp32 row statistics).\n")
+
     log(f"wrote profiles: prefill {pavg:.1f} us ({ptf:.0f} TFLOP/s), decode {davg:.1f} us ({dgbs:.0f} GB/s), "
         f"traffic {traffic['prefill'][2] / 1e6:.1f} / {traffic['decode'][2] / 1e6:.1f} MB")
 
