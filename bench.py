@@ -21,8 +21,9 @@ sustained rate of K prefill launches in a row is reported beside it
 (informational): with no decode between them the chip holds its matrix load
 and lowers its clock.
 
-After the timed steps, the next rows of the path are timed the same way
-(informational, under "next"): the backward pass of the prefill workload,
+After the timed steps, the other prefill workloads and the next rows of the
+path are timed (informational), each as back-to-back calls after untimed
+calls for half the settle time; under "next": the backward pass of the prefill workload,
 decode over an int4 cache of the decode workload's shape, a packed
 variable-length prefill, decode with per-sequence cache lengths, and the
 int8 / int4 cache append of one 32K-token tensor.
@@ -446,22 +447,33 @@ def main():
         del csrc, cdst
         torch.cuda.empty_cache()
 
+    def time_calls(fn, reps=10):
+        """Average µs per call of fn over reps back-to-back calls, after calls
+        for half the settle time (the clocks drop while the host prepares the
+        inputs) and three warmup calls."""
+        t_end = time.perf_counter() + args.settle_ms / 2e3
+        while time.perf_counter() < t_end:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
     if do_prefill and args.only == "all":
         # the other prefill workloads, informational (same kernel, same timing method)
         others = {}
         for w in (W.GQA_CAUSAL, W.MQA_CAUSAL, W.MQA_WINDOW):
             qq, kk, vv = (t.to(dev) for t in W.workload_inputs(w))
             oo = torch.empty_like(qq)
-            for _ in range(3):
-                fa.fwd(qq, kk, vv, causal=w.causal, window=w.window, scale=w.scale, out=oo)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 20
-            e0.record(stream)
-            for _ in range(reps):
-                fa.fwd(qq, kk, vv, causal=w.causal, window=w.window, scale=w.scale, out=oo)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            us = time_calls(lambda: fa.fwd(qq, kk, vv, causal=w.causal, window=w.window, scale=w.scale, out=oo),
+                            reps=20)
             tf = prefill_flops(w) / (us * 1e-6) / 1e12
             others[w.name] = {"us": round(us, 2), "TFLOP/s": round(tf, 2),
                               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
@@ -473,17 +485,6 @@ def main():
         result["next"] = {}
         del dq, dkq, dks, dvq, dvs, dcache
         torch.cuda.empty_cache()
-
-        def time_calls(fn, reps=10):
-            for _ in range(3):
-                fn()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / reps
 
         def hbm_entry(workload, us, nbytes):
             return {"workload": workload, "us": round(us, 2),
