@@ -57,7 +57,9 @@ typedef enum {
                              Hq % Hkv != 0, an append past the cache end, a
                              non-finite scale, causal not 0/1, window < 0,
                              window > 0 without causal, num_splits < 0, or a
-                             tensor too large to index */
+                             tensor too large to index (the prefill and
+                             backward also need Hq*d < 2^24 and Hkv*d
+                             < 2^25: 32-bit offsets inside a tile) */
   FATTN_EUNSUPPORTED = -2, /* head_dim or dtype outside what the kernels cover */
   FATTN_EWORKSPACE = -3,  /* workspace NULL or smaller than the size query */
   FATTN_EHIP = -4         /* the HIP runtime refused a kernel launch */

@@ -368,13 +368,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   // ---- dQ = scale * (K^T dS^T)^T, bf16 (RNE), written as whole rows through
   // the stage the last step did not read (idle once that step's barrier has
   // passed; each wave uses its own quarter)
-  store_tile_rows_bf16<D>(lds + (ntiles & 1) * STAGE_B + w * 32 * ROWB, acc, p.scale,
-                          [&](int r) -> __bf16* {
+  char* qbase = reinterpret_cast<char*>(p.dq + ((int64_t(b) * Sq + p0) * p.Hq + hq0) * D);
+  store_tile_rows_bf16<D>(lds + (ntiles & 1) * STAGE_B + w * 32 * ROWB, acc, p.scale, qbase,
+                          [&](int r) -> uint32_t {
                             const int prow = w * 32 + r;
-                            const int ppos = p0 + (prow >> p.gc_shift);
-                            return ppos < Sq ? p.dq + ((int64_t(b) * Sq + ppos) * p.Hq + hq0 +
-                                                       (prow & (gc - 1))) * D
-                                             : nullptr;
+                            const int dpos = prow >> p.gc_shift;
+                            return p0 + dpos < Sq
+                                       ? uint32_t(dpos * p.Hq + (prow & (gc - 1))) * uint32_t(2 * D)
+                                       : kSkipRow;
                           });
 }
 
@@ -731,12 +732,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   // that step's barrier has passed; each wave uses its own quarter, first for
   // dK, then for dV)
   char* stage = lds + (niter & 1) * STAGE_B + w * 32 * ROWB;
-  store_tile_rows_bf16<D>(stage, acck, p.scale, [&](int r) -> __bf16* {
-    return jw + r < Skv ? p.dk + ((int64_t(b) * Skv + jw + r) * p.Hkv + hk) * D : nullptr;
-  });
-  store_tile_rows_bf16<D>(stage, accv, 1.f, [&](int r) -> __bf16* {
-    return jw + r < Skv ? p.dv + ((int64_t(b) * Skv + jw + r) * p.Hkv + hk) * D : nullptr;
-  });
+  const int64_t kvrow0 = (int64_t(b) * Skv + jw) * p.Hkv + hk;  // this wave's first key row
+  auto key_off = [&](int r) -> uint32_t {
+    return jw + r < Skv ? uint32_t(r * p.Hkv) * uint32_t(2 * D) : kSkipRow;
+  };
+  store_tile_rows_bf16<D>(stage, acck, p.scale, reinterpret_cast<char*>(p.dk + kvrow0 * D), key_off);
+  store_tile_rows_bf16<D>(stage, accv, 1.f, reinterpret_cast<char*>(p.dv + kvrow0 * D), key_off);
 }
 
 // Sums the head-split partials of dK and dV in split order -> bf16; 8

@@ -152,11 +152,15 @@ __device__ __forceinline__ int swz(int r) {
 // sixteen 8-byte pieces of 32 different rows per lane.  16-byte chunks are
 // XOR-swizzled by row so that neither the 8-byte writes (one chunk of 32 rows)
 // nor the 16-byte reads (whole rows) conflict in the LDS banks.  The global
-// stores carry the non-temporal hint.  row_ptr(r)
-// gives the output address of tile row r, or nullptr to skip it.
-template <int D, class RowPtr>
-__device__ __forceinline__ void store_tile_rows_bf16(char* stage, const f32x16* acc, float mul,
-                                                     RowPtr row_ptr) {
+// stores carry the non-temporal hint.  Tile row r goes to base + row_off(r)
+// bytes, or nowhere if row_off(r) is kSkipRow; base is the same for the whole
+// wave and the offsets are 32-bit, so each store addresses a scalar base plus
+// a lane offset (measured on MI355X: the d = 64 prefill's epilogue issues
+// about a third fewer vector instructions than with a 64-bit address per row).
+constexpr uint32_t kSkipRow = 0xffffffffu;
+template <int D, class RowOff>
+__device__ __forceinline__ void store_tile_rows_bf16(char* stage, const f32x16* acc, float mul, char* base,
+                                                     RowOff row_off) {
   constexpr int ROWB = 2 * D, KCH = D / 8, NB = D / 32, RPI = 1024 / ROWB;
   static_assert(D == 64 || D == 128, "head dims of the kernels");
   const int lane = threadIdx.x & 63, lq = lane & 31, hh = lane >> 5;
@@ -177,8 +181,8 @@ __device__ __forceinline__ void store_tile_rows_bf16(char* stage, const f32x16* 
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = i * RPI + lane / KCH, c = lane % KCH;
     const uint4 v = *reinterpret_cast<const uint4*>(stage + r * ROWB + ((c ^ cswz(r)) << 4));
-    __bf16* dst = row_ptr(r);
-    if (dst) store_nt16(dst + c * 8, v);  // written once, read by a later kernel
+    const uint32_t off = row_off(r);
+    if (off != kSkipRow) store_nt16(base + (off + uint32_t(c) * 16u), v);  // read by a later kernel
   }
 }
 

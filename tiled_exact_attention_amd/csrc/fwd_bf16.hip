@@ -175,12 +175,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   bf16x8 qf[KSTEPS];
   {
     const __bf16* qrow = p.q + ((sv.q_row0 + (row_ok ? pos : 0)) * p.Hq + hq) * D;
+    const uint32_t sign = p.negate ? 0x80008000u : 0u;  // uniform: one xor per dword
 #pragma unroll
     for (int m = 0; m < KSTEPS; ++m) {
       uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * m + 8 * hh);
-      if (p.negate) {
-        raw.x ^= 0x80008000u; raw.y ^= 0x80008000u; raw.z ^= 0x80008000u; raw.w ^= 0x80008000u;
-      }
+      raw.x ^= sign; raw.y ^= sign; raw.z ^= sign; raw.w ^= sign;
       qf[m] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -359,9 +358,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       return ps;
     };
     if constexpr (decltype(first)::value) {
-      // first tile: the reference is the row max
-      const float mx = raise_reference();
-      if (__any(mx > m_run + kLazy)) rescale_to(fmaxf(m_run, mx));
+      // first tile of the wave: the reference is the row max (the accumulator
+      // and the row sum are still zero, so nothing is rescaled)
+      m_run = fmaxf(m_run, raise_reference());
       l_run += exponentials();
     } else {
       // later tiles keep the reference unless some exponential exceeds 2^kLazy,
@@ -384,10 +383,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // P(ntiles-1)^T; every other one does both, so the steady state has no
   // branches.  Every wave takes every tile of the block's band: keys a row
   // cannot see get probability exactly 0.  Tiles [t_lo, t_hi) are fully
-  // visible to every row of the block and skip the mask; tile 0, the tiles
-  // before t_lo (window edge) and from t_hi on (causal edge, end of the
-  // keys) are masked.  Iterations run in pairs (odd t, then even t) so the
-  // buffer offsets are compile-time constants.
+  // visible to every row of the block and skip the mask; the tiles before
+  // t_lo (window edge) and from t_hi on (causal edge, end of the keys) are
+  // masked, and so is tile 0 unless every row sees all of it.  Iterations
+  // run in pairs (odd t, then even t) so the buffer offsets are
+  // compile-time constants.
   auto begin = [&](int t, char* knxt, char* vcur) __attribute__((always_inline)) {
     wait_vmcnt<0>();   // this wave's copies of K(t) and V(t-1) have landed
     __syncthreads();   // ... and everyone's; everyone has left iteration t-1
@@ -408,11 +408,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   };
   if (ntiles > 0) {
     int t_lo, t_hi;  // odd, t_lo <= t_hi, t_hi - t_lo even
+    bool first_full;  // tile 0 fully visible to every row (no mask)
     {
       const int64_t hi_min = p.causal ? min(int64_t(Skv), p0 + off + 1) : int64_t(Skv);
       const int64_t lo_max = (p.causal && p.window > 0) ? max(int64_t(0), bpos_hi + off - p.window + 1) : 0;
       const int raw_hi = hi_min - jb >= kBN ? int(min(int64_t(ntiles), (hi_min - jb) / kBN)) : 0;
       const int raw_lo = lo_max > jb ? int(min(int64_t(raw_hi), (lo_max - jb + kBN - 1) / kBN)) : 0;
+      first_full = raw_lo == 0 && raw_hi >= 1;
       t_lo = max(raw_lo, 1) | 1;
       t_hi = raw_hi > t_lo ? t_lo + ((raw_hi - t_lo) & ~1) : t_lo;
     }
@@ -420,20 +422,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     {
       const int64_t j0 = begin(0, lds + TILE_B, lds + 2 * TILE_B);
       products(lds, lds, std::true_type{}, std::false_type{});
-      softmax(j0, std::true_type{}, std::true_type{});
+      if (first_full) {
+        softmax(j0, std::false_type{}, std::true_type{});
+      } else {
+        softmax(j0, std::true_type{}, std::true_type{});
+      }
     }
     int t = 1;
     for (; t < t_lo && t < ntiles; t += 2) pair(t, std::true_type{});
     for (; t < t_hi; t += 2) pair(t, std::false_type{});
     for (; t < ntiles; t += 2) pair(t, std::true_type{});
-    // last product: V(ntiles-1) sits in V buffer (ntiles-1) % 2
-    if (ntiles & 1) {
-      begin(ntiles, lds, lds);
-      products(lds, lds + 2 * TILE_B, std::false_type{}, std::true_type{});
-    } else {
-      begin(ntiles, lds, lds);
-      products(lds, lds + 3 * TILE_B, std::false_type{}, std::true_type{});
-    }
+    // last product: V(ntiles-1) sits in V buffer (ntiles-1) % 2 (one code
+    // path, so the accumulators leave the loop in the same registers)
+    begin(ntiles, lds, lds);
+    products(lds, lds + (2 + ((ntiles - 1) & 1)) * TILE_B, std::false_type{}, std::true_type{});
   }
 
   // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log).
@@ -444,10 +446,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // went from about 2.7 to 1.8 us).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  store_tile_rows_bf16<D>(lds + w * 32 * ROWB, acc, inv, [&](int r) -> __bf16* {
+  // rows of the block start at (position p0, head hq0); a row's byte offset
+  // from there is below 2^32 (128 positions of Hq * d elements, checked on
+  // the host)
+  char* obase = reinterpret_cast<char*>(p.o + ((sv.q_row0 + p0) * p.Hq + hq0) * D);
+  store_tile_rows_bf16<D>(lds + w * 32 * ROWB, acc, inv, obase, [&](int r) -> uint32_t {
     const int prow = w * 32 + r;
-    const int ppos = p0 + (prow >> p.gc_shift);
-    return ppos < Sq ? p.o + ((sv.q_row0 + ppos) * p.Hq + hq0 + (prow & (gc - 1))) * D : nullptr;
+    const int dpos = prow >> p.gc_shift;
+    return p0 + dpos < Sq ? uint32_t(dpos * p.Hq + (prow & (gc - 1))) * uint32_t(2 * D) : kSkipRow;
   });
   if (!row_ok) return;
   if (hh == 0 && p.lse) {
