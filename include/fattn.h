@@ -212,15 +212,18 @@ FATTN_API int fattn_decode_int8(const void* q, const int8_t* kq, const float* k_
  * library instead of a caller workspace: 32 MiB per GPU, allocated when the
  * library's code is loaded on that GPU and held until the process ends; with
  * at most 8 splits nothing beyond o and lse is touched.  Besides its kernel
- * launches the call makes hipGetDevice and, on its first use of a device,
- * hipGetSymbolAddress; it allocates nothing.  Every call on one GPU shares
+ * launches the call asks which GPU runs the stream (hipStreamGetDevice, or
+ * hipGetDevice for the null stream) and, on its first use of that GPU, takes
+ * the array's address there (hipGetSymbolAddress, with the GPU made current
+ * for that call and the caller's current device restored); it allocates
+ * nothing.  Every call on one GPU shares
  * that GPU's scratch, which keeps the last call's contents (nothing in it has
  * to start at zero): calls that use it and overlap on one GPU (other streams,
  * other host threads) race and must be serialised by the caller.
  *
  * Errors as fattn_decode_int8, plus FATTN_EWORKSPACE when the plan's partials
  * (fattn_decode_workspace_size for the same arguments) exceed the 32 MiB, and
- * FATTN_EHIP when the scratch address cannot be obtained on the current device.
+ * FATTN_EHIP when the scratch address cannot be obtained on the stream's GPU.
  */
 FATTN_API int fattn_decode_int8_noalloc(const void* q, const int8_t* kq, const float* k_scale,
                       const int8_t* vq, const float* v_scale, void* o, float* lse,

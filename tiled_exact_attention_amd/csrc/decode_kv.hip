@@ -597,17 +597,28 @@ std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once taken
 }  // namespace
 
-hipError_t decode_scratch(void** ptr) {
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  // the GPU the kernels will run on: the stream's (the null stream is the
+  // current device's)
   int dev = -1;
-  hipError_t err = hipGetDevice(&dev);
+  hipError_t err = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     // the array's name is a host-side stand-in: only this address may be
-    // handed to kernels (each device holds its own copy at its own address)
+    // handed to kernels (each device holds its own copy at its own address),
+    // and it is taken with that device current
+    int cur = -1;
+    err = hipGetDevice(&cur);
+    if (err != hipSuccess) return err;
+    if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return err;
     void* p = nullptr;
     err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (err == hipSuccess) err = back;
+    }
     if (err != hipSuccess) return err;
     if (!p) return hipErrorInvalidSymbol;
     g_scratch_ptr[dev] = p;

@@ -128,7 +128,7 @@ int decode(const void* q, const void* kq, const float* k_scale, const void* vq,
     // only plans that merge through partials touch memory beyond o and lse
     workspace = nullptr;
     if (nsplit > fattn::kDecodeWgMaxSplits) {
-      if (fattn::decode_scratch(&workspace) != hipSuccess) return FATTN_EHIP;
+      if (fattn::decode_scratch(static_cast<hipStream_t>(stream), &workspace) != hipSuccess) return FATTN_EHIP;
     }
   } else if (!workspace || workspace_bytes < need || !aligned16(workspace)) {
     return FATTN_EWORKSPACE;

@@ -100,9 +100,9 @@ constexpr int kDecodeWgMaxSplits = 8;
 // ends), used instead of a caller workspace by fattn_decode_int8_noalloc.
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 
-// Device address of the built-in scratch array on the current device
-// (hipGetSymbolAddress, taken once per device and kept).
-hipError_t decode_scratch(void** ptr);
+// Device address of the built-in scratch array on the GPU that runs `stream`
+// (hipGetSymbolAddress with that GPU current, taken once per device and kept).
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
 
 // Enqueues kernel<<<grid, block, lds, stream>>>(args...) and returns the
 // status of that launch itself (hipLaunchKernel's result), never an error
