@@ -139,6 +139,8 @@ def _fwd(**kw):
     (dict(B=1 << 20, Hq=1 << 10, Hkv=1, Sq=1 << 12, Skv=4), FATTN_EINVAL),
     # a 64-key tile of 2^18 kv heads x 128 no longer fits 32-bit offsets
     (dict(Hq=1 << 18, Hkv=1 << 18, Sq=1, Skv=1, d=128), FATTN_EINVAL),
+    # ... nor do 128 output rows of 2^17 query heads x 128 (one kv head)
+    (dict(Hq=1 << 17, Hkv=1, Sq=1, Skv=1, d=128), FATTN_EINVAL),
 ])
 def test_fwd_rejects_before_any_device_work(kw, want):
     assert _fwd(**kw) == want
@@ -273,6 +275,7 @@ def _bwd(**kw):
     (dict(scale=math.inf), FATTN_EINVAL), (dict(window=3, causal=0), FATTN_EINVAL),
     (dict(dtype=0), FATTN_EUNSUPPORTED), (dict(d=96), FATTN_EUNSUPPORTED),
     (dict(ws=None), FATTN_EWORKSPACE), (dict(ws=P + 8), FATTN_EWORKSPACE), (dict(ws_bytes=16), FATTN_EWORKSPACE),
+    (dict(Hq=1 << 17, Hkv=1, Sq=1, Skv=1, d=128), FATTN_EINVAL),  # output rows past 32-bit offsets
 ])
 def test_bwd_rejects_before_any_device_work(kw, want):
     assert _bwd(**kw) == want
