@@ -236,6 +236,7 @@ def _fwdv(**kw):
     (dict(tq=0, mq=0), FATTN_OK),  # an empty batch is valid and launches nothing
     (dict(tq=0, mq=0, q=None, o=None), FATTN_OK),  # ... also with null (empty) tensors
     (dict(k=None), FATTN_EINVAL), (dict(v=None), FATTN_EINVAL),  # keys present, no k / v
+    (dict(Hq=1 << 17, Hkv=1, d=128), FATTN_EINVAL),  # output rows past 32-bit offsets
 ])
 def test_fwd_varlen_rejects_before_any_device_work(kw, want):
     assert _fwdv(**kw) == want
