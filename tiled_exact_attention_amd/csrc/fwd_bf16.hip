@@ -388,18 +388,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // masked, and so is tile 0 unless every row sees all of it.  Iterations
   // run in pairs (odd t, then even t) so the buffer offsets are
   // compile-time constants.
-  auto begin = [&](int t, char* knxt, char* vcur) __attribute__((always_inline)) {
+  // The copies of iteration t are issued after its products, not before:
+  // while LDS-DMA copies are in flight the compiler can neither prove that
+  // the operand reads miss their destinations (it waits for the copies,
+  // vmcnt(0), before the first V^T read) nor count LDS reads precisely (it
+  // waits for every outstanding read, lgkmcnt(0)); issued after the products
+  // they overlap the softmax and the barrier, and the products run with
+  // exact waits.
+  auto begin = [&](int t) __attribute__((always_inline)) {
     wait_vmcnt<0>();   // this wave's copies of K(t) and V(t-1) have landed
     __syncthreads();   // ... and everyone's; everyone has left iteration t-1
-    const int64_t j0 = jb + int64_t(t) * kBN;
+    return jb + int64_t(t) * kBN;
+  };
+  auto copies = [&](int t, int64_t j0, char* knxt, char* vcur) __attribute__((always_inline)) {
     if (t + 1 < ntiles) issue_tile(kbase, j0 + kBN, knxt);
     if (t < ntiles) issue_tile(vbase, j0, vcur);
-    return j0;
   };
   auto iteration = [&](int t, auto odd, auto masked) __attribute__((always_inline)) {
     constexpr int cur = decltype(odd)::value ? 1 : 0;
-    const int64_t j0 = begin(t, lds + (cur ^ 1) * TILE_B, lds + (2 + cur) * TILE_B);
+    const int64_t j0 = begin(t);
     products(lds + cur * TILE_B, lds + (2 + (cur ^ 1)) * TILE_B, std::true_type{}, std::true_type{});
+    copies(t, j0, lds + (cur ^ 1) * TILE_B, lds + (2 + cur) * TILE_B);
     softmax(j0, masked, std::false_type{});
   };
   auto pair = [&](int t, auto masked) __attribute__((always_inline)) {
@@ -420,8 +429,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     }
     issue_tile(kbase, jb, lds);
     {
-      const int64_t j0 = begin(0, lds + TILE_B, lds + 2 * TILE_B);
+      const int64_t j0 = begin(0);
       products(lds, lds, std::true_type{}, std::false_type{});
+      copies(0, j0, lds + TILE_B, lds + 2 * TILE_B);
       if (first_full) {
         softmax(j0, std::false_type{}, std::true_type{});
       } else {
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     for (; t < ntiles; t += 2) pair(t, std::true_type{});
     // last product: V(ntiles-1) sits in V buffer (ntiles-1) % 2 (one code
     // path, so the accumulators leave the loop in the same registers)
-    begin(ntiles, lds, lds);
+    begin(ntiles);
     products(lds, lds + (2 + ((ntiles - 1) & 1)) * TILE_B, std::false_type{}, std::true_type{});
   }
 
