@@ -231,15 +231,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const __bf16* vbase = p.v + (int64_t(b) * Skv * p.Hkv + hk) * D;
   // (source offsets are recomputed per tile rather than kept in registers)
   auto issue_loads = [&](int64_t j0, char* stage) __attribute__((always_inline)) {
+    const __bf16* kt = kbase + j0 * kv_stride;
+    const __bf16* vt = vbase + j0 * kv_stride;
+    // at d = 128 the lane terms are recomputed here, not held across the
+    // loop (held, they spill at 256 registers); at d = 64 holding them is
+    // faster
+    int ln = lane;
+    if constexpr (D >= 128) asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int r = 16 * w + LPI * i + lane / KCH;
+      const int r = 16 * w + LPI * i + ln / KCH;
       // rows past the end of the keys re-read the last row
-      const int64_t j = min(j0 + r, int64_t(Skv) - 1);
-      const int64_t e = j * kv_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
+      const int jr = int(min(j0 + r, int64_t(Skv) - 1) - j0);
+      const uint32_t e = (uint32_t(jr) * uint32_t(kv_stride) + ((ln % KCH) ^ swz<D>(r)) * 8) * 2u;
       char* dst = stage + (16 * w + LPI * i) * ROWB;
-      global_to_lds16(kbase + e, dst);
-      global_to_lds16(vbase + e, dst + TILE_B);
+      buffer_to_lds16(kt, e, dst);
+      buffer_to_lds16(vt, e, dst + TILE_B);
     }
   };
 
@@ -470,13 +477,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   // 16w .. 16w+15 of the Q and dO tiles; waves 0 and 1 also fetch the 64
   // lse2 and D values
   const int64_t q_stride = int64_t(p.Hq) * D;
-  int64_t goff[NLD];
+  uint32_t goff[NLD];  // element offsets within a tile (below 2^31: Hq * d < 2^24)
   int ld_row[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
     const int r = 16 * w + LPI * i + lane / KCH;
     ld_row[i] = r;
-    goff[i] = int64_t(r) * q_stride + ((lane % KCH) ^ swz<D>(r)) * 8;
+    goff[i] = uint32_t(r) * uint32_t(q_stride) + ((lane % KCH) ^ swz<D>(r)) * 8;
   }
   auto issue_loads = [&](int it, char* stage) __attribute__((always_inline)) {
     const int g = g0 + it / ntq;
@@ -484,27 +491,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int hq = hk * p.G + g;
     const __bf16* qb = p.q + (int64_t(b) * Sq * p.Hq + hq) * D;
     const __bf16* db = p.dout + (int64_t(b) * Sq * p.Hq + hq) * D;
+    const __bf16* qt = qb + int64_t(i0) * q_stride;
+    const __bf16* dt = db + int64_t(i0) * q_stride;
     if (i0 + kBQ <= Sq) {
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         char* dst = stage + (16 * w + LPI * i) * ROWB;
-        global_to_lds16(qb + int64_t(i0) * q_stride + goff[i], dst);
-        global_to_lds16(db + int64_t(i0) * q_stride + goff[i], dst + TILE_B);
+        buffer_to_lds16(qt, goff[i] * 2u, dst);
+        buffer_to_lds16(dt, goff[i] * 2u, dst + TILE_B);
       }
     } else {
       // last tile of the queries: rows past the end re-read the last row
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int64_t r = min(int64_t(i0) + ld_row[i], int64_t(Sq) - 1);
-        const int64_t e = goff[i] + (r - ld_row[i]) * q_stride;
+        const int back = max(i0 + ld_row[i] - (Sq - 1), 0);
+        const uint32_t e = (goff[i] - uint32_t(back) * uint32_t(q_stride)) * 2u;
         char* dst = stage + (16 * w + LPI * i) * ROWB;
-        global_to_lds16(qb + e, dst);
-        global_to_lds16(db + e, dst + TILE_B);
+        buffer_to_lds16(qt, e, dst);
+        buffer_to_lds16(dt, e, dst + TILE_B);
       }
     }
     if (w < 2) {
-      const float* src = (w == 0 ? p.l2 : p.dd) + (int64_t(b) * p.Hq + hq) * Sq;
-      global_to_lds4(src + min(i0 + lane, Sq - 1), stage + 2 * TILE_B + w * (kBQ * 4));
+      const float* src = (w == 0 ? p.l2 : p.dd) + (int64_t(b) * p.Hq + hq) * Sq + i0;
+      buffer_to_lds4(src, uint32_t(min(lane, Sq - 1 - i0)) * 4u, stage + 2 * TILE_B + w * (kBQ * 4));
     }
   };
 

@@ -111,9 +111,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   constexpr int NB = D / 32;                 // 32-wide blocks of the output row
   static_assert(NLD * LPI * kWaves == kBN, "tile rows must split evenly over the waves");
   static_assert(4 * TILE_B <= 65536, "LDS read offsets fit the 16-bit immediate");
-  // LDS: K buffers 0 and 1, then V buffers 0 and 1 (the K buffers also stage
-  // the output rows in the epilogue)
-  __shared__ __attribute__((aligned(1024))) char lds[4 * TILE_B];
+  // LDS: two K buffers and two V buffers, one tile each (the K buffers also
+  // stage the output rows in the epilogue)
+  __shared__ __attribute__((aligned(1024))) char lds_k0[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[TILE_B];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[TILE_B];
+  char* const kbuf[2] = {lds_k0, lds_k1};
+  char* const vbuf[2] = {lds_v0, lds_v1};
 
   // ---- block -> (batch, kv head, head chunk, query block); heavy blocks first.
   // Workgroups go to the 8 XCDs round-robin (id % 8).  Dense batches number
@@ -230,14 +235,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     const char* src = reinterpret_cast<const char*>(base + j0 * kv_stride);
     if (j0 + kBN <= Skv) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) global_to_lds16(src + goff[i], dst_tile + (16 * w + LPI * i) * ROWB);
+      for (int i = 0; i < NLD; ++i)
+        buffer_to_lds16(src, goff[i], dst_tile + (16 * w + LPI * i) * ROWB);
     } else {
       const int last = int(Skv - 1 - j0);  // last row of the sequence within this tile
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
         const int r = 16 * w + LPI * i + lr;
         const uint32_t back = uint32_t(max(r - last, 0)) * row_b;
-        global_to_lds16(src + (goff[i] - back), dst_tile + (16 * w + LPI * i) * ROWB);
+        buffer_to_lds16(src, goff[i] - back, dst_tile + (16 * w + LPI * i) * ROWB);
       }
     }
   };
@@ -388,13 +394,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // masked, and so is tile 0 unless every row sees all of it.  Iterations
   // run in pairs (odd t, then even t) so the buffer offsets are
   // compile-time constants.
-  // The copies of iteration t are issued after its products, not before:
-  // while LDS-DMA copies are in flight the compiler can neither prove that
-  // the operand reads miss their destinations (it waits for the copies,
-  // vmcnt(0), before the first V^T read) nor count LDS reads precisely (it
-  // waits for every outstanding read, lgkmcnt(0)); issued after the products
-  // they overlap the softmax and the barrier, and the products run with
-  // exact waits.
+  // The copies are issued in buffer form (buffer_load ... lds): for the flat
+  // form the compiler cannot prove that the operand reads miss the copies'
+  // destinations (it waits for the copies, vmcnt(0), before the first V^T
+  // read) and stops counting LDS reads precisely (every wait becomes
+  // lgkmcnt(0)); the buffer form keeps both waits exact.  The copies of
+  // iteration t go out after its products, so that the products start at
+  // once and the copies overlap the softmax and the barrier; measured on
+  // MI355X that order is the faster one for every head layout.
   auto begin = [&](int t) __attribute__((always_inline)) {
     wait_vmcnt<0>();   // this wave's copies of K(t) and V(t-1) have landed
     __syncthreads();   // ... and everyone's; everyone has left iteration t-1
@@ -407,8 +414,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   auto iteration = [&](int t, auto odd, auto masked) __attribute__((always_inline)) {
     constexpr int cur = decltype(odd)::value ? 1 : 0;
     const int64_t j0 = begin(t);
-    products(lds + cur * TILE_B, lds + (2 + (cur ^ 1)) * TILE_B, std::true_type{}, std::true_type{});
-    copies(t, j0, lds + (cur ^ 1) * TILE_B, lds + (2 + cur) * TILE_B);
+    products(kbuf[cur], vbuf[cur ^ 1], std::true_type{}, std::true_type{});
+    copies(t, j0, kbuf[cur ^ 1], vbuf[cur]);
     softmax(j0, masked, std::false_type{});
   };
   auto pair = [&](int t, auto masked) __attribute__((always_inline)) {
@@ -427,11 +434,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       t_lo = max(raw_lo, 1) | 1;
       t_hi = raw_hi > t_lo ? t_lo + ((raw_hi - t_lo) & ~1) : t_lo;
     }
-    issue_tile(kbase, jb, lds);
+    issue_tile(kbase, jb, lds_k0);
     {
       const int64_t j0 = begin(0);
-      products(lds, lds, std::true_type{}, std::false_type{});
-      copies(0, j0, lds + TILE_B, lds + 2 * TILE_B);
+      products(lds_k0, lds_v0, std::true_type{}, std::false_type{});
+      copies(0, j0, lds_k1, lds_v0);
       if (first_full) {
         softmax(j0, std::false_type{}, std::true_type{});
       } else {
@@ -445,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     // last product: V(ntiles-1) sits in V buffer (ntiles-1) % 2 (one code
     // path, so the accumulators leave the loop in the same registers)
     begin(ntiles);
-    products(lds, lds + (2 + ((ntiles - 1) & 1)) * TILE_B, std::false_type{}, std::true_type{});
+    products(lds_k0, ((ntiles - 1) & 1) ? lds_v1 : lds_v0, std::false_type{}, std::true_type{});
   }
 
   // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log).
@@ -460,7 +467,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // from there is below 2^32 (128 positions of Hq * d elements, checked on
   // the host)
   char* obase = reinterpret_cast<char*>(p.o + ((sv.q_row0 + p0) * p.Hq + hq0) * D);
-  store_tile_rows_bf16<D>(lds + w * 32 * ROWB, acc, inv, obase, [&](int r) -> uint32_t {
+  const int so = w * 32 * ROWB;  // this wave's staging rows: K buffer 0, then K buffer 1
+  store_tile_rows_bf16<D>(so < TILE_B ? lds_k0 + so : lds_k1 + (so - TILE_B), acc, inv, obase,
+                          [&](int r) -> uint32_t {
     const int prow = w * 32 + r;
     const int dpos = prow >> p.gc_shift;
     return p0 + dpos < Sq ? uint32_t(dpos * p.Hq + (prow & (gc - 1))) * uint32_t(2 * D) : kSkipRow;
