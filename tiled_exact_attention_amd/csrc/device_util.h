@@ -64,35 +64,25 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Asynchronous 16-byte-per-lane copy HBM -> LDS (global_load_lds_dwordx4):
-// lane l's 16 bytes from gsrc land at lds_dst + 16*l; lds_dst must be the same
-// for every lane of the wave.  Completion is tracked by vmcnt (wait_vmcnt).
-__device__ __forceinline__ void global_to_lds16(const void* gsrc, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(
-      (const __attribute__((address_space(1))) void*)(gsrc),
-      (__attribute__((address_space(3))) void*)(lds_dst), 16, 0, 0);
-}
-
-// The same 16-byte-per-lane copy in its buffer form (buffer_load_dwordx4 ... lds):
-// lane l's 16 bytes from base + voff land at lds_dst + 16*l.  base and lds_dst
-// must be uniform over the wave; voff is per lane.  The resource descriptor is
-// raw (stride 0, no range limit that a byte offset below 4 GiB can reach).
-// Unlike the flat form, the compiler's wait tracking keeps this copy on vmcnt
-// alone, so LDS reads of other buffers issued after it get exact lgkmcnt waits.
+// Asynchronous 16-byte-per-lane copy HBM -> LDS in buffer form
+// (buffer_load_dwordx4 ... lds): lane l's 16 bytes from base + voff land at
+// lds_dst + 16*l.  base and lds_dst must be uniform over the wave; voff is per
+// lane.  The resource descriptor is raw: stride 0, a record count no byte
+// offset below 4 GiB reaches, and word 3 = 0x00020000 (data format 32 bits; a
+// zero data format makes gfx9 treat every access as out of range).
+// Completion is tracked by vmcnt (wait_vmcnt).
+// The flat form (global_load_lds_dwordx4) does the same copy, but while one is
+// in flight the compiler assumes any LDS read may alias it (waiting for the
+// copies before reads of other buffers) and stops counting LDS reads exactly
+// (every LDS wait becomes lgkmcnt(0)); the buffer form keeps both waits exact.
 __device__ __forceinline__ void buffer_to_lds16(const void* base, uint32_t voff, void* lds_dst) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, FATTN_LDS(void, lds_dst), 16, voff, 0, 0, 0);
 }
 
-// Asynchronous 4-byte-per-lane copy HBM -> LDS (global_load_lds_dword).
-__device__ __forceinline__ void global_to_lds4(const void* gsrc, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(
-      (const __attribute__((address_space(1))) void*)(gsrc),
-      (__attribute__((address_space(3))) void*)(lds_dst), 4, 0, 0);
-}
-
-// Its buffer form: lane l's 4 bytes from base + voff land at lds_dst + 4*l.
+// The 4-byte-per-lane copy (buffer_load_dword ... lds): lane l's 4 bytes from
+// base + voff land at lds_dst + 4*l.
 __device__ __forceinline__ void buffer_to_lds4(const void* base, uint32_t voff, void* lds_dst) {
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0xffffffff, 0x00020000);

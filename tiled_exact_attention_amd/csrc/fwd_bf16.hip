@@ -21,7 +21,7 @@
 //  * V^T is read from a row-major V tile with ds_read_b64_tr_b16, the
 //    transposing LDS read, in the key order the P layout dictates.
 //  * K/V tiles of 64 keys are filled straight from HBM into LDS by
-//    global_load_lds_dwordx4 (no register staging), two K and two V buffers.
+//    buffer_load_dwordx4 ... lds (no register staging), two K and two V buffers.
 //    Each wave is software-pipelined by one tile: iteration t multiplies
 //    S(t) = K(t) Q^T and O += V(t-1)^T P(t-1) in one block of matrix
 //    products, then turns S(t) into P(t).  The products of one iteration are
