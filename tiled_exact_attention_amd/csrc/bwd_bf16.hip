@@ -326,7 +326,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     for (int kc = 0; kc < 4; ++kc) {
       float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = float(pf[kc][i]) * (dp[kc >> 1][8 * (kc & 1) + i] - dd);
+      for (int i = 0; i < 8; ++i) {
+        // element i of pf[kc] widened to fp32 from its packed dword (pf stays
+        // packed: one conversion per pair of probabilities, not per element)
+        const uint32_t pw = __builtin_bit_cast(u32x4, pf[kc])[i / 2];
+        e[i] = __builtin_bit_cast(float, (i & 1) ? (pw & 0xffff0000u) : (pw << 16)) *
+               (dp[kc >> 1][8 * (kc & 1) + i] - dd);
+      }
       dsf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
     __builtin_amdgcn_s_setprio(1);
