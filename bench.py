@@ -478,6 +478,16 @@ def main():
             others[w.name] = {"us": round(us, 2), "TFLOP/s": round(tf, 2),
                               "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
             del qq, kk, vv, oo
+        # long dense rows: the loop rate without the causal launch's short
+        # blocks and masked tiles (informational)
+        wl = W.MHA_DENSE_LONG
+        qq, kk, vv = W.workload_inputs(wl, device=dev)
+        oo = torch.empty_like(qq)
+        us = time_calls(lambda: fa.fwd(qq, kk, vv, causal=False, scale=wl.scale, out=oo), reps=5)
+        tf = prefill_flops(wl) / (us * 1e-6) / 1e12
+        others[wl.name] = {"us": round(us, 2), "TFLOP/s": round(tf, 2), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                           "note": "loop rate on long unmasked rows; not a parity configuration"}
+        del qq, kk, vv, oo
         result["prefill_other_workloads"] = others
 
     if args.only == "all":

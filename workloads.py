@@ -68,6 +68,9 @@ MHA_CAUSAL = Prefill("MHA causal prefill bf16 B2 H32 S4096 d128", 2, 32, 32, 409
 GQA_CAUSAL = Prefill("GQA causal prefill bf16 B1 Hq32 Hkv8 S4096 d128", 1, 32, 8, 4096, 4096, 128, True, 0, "bf16", 2)
 MQA_CAUSAL = Prefill("MQA causal prefill bf16 B1 Hq232 Hkv1 S2048 d64", 1, 232, 1, 2048, 2048, 64, True, 0, "bf16", 3)
 MQA_WINDOW = Prefill("MQA causal sliding-window-512 prefill bf16 B1 Hq232 Hkv1 S2048 d64", 1, 232, 1, 2048, 2048, 64, True, 512, "bf16", 3)
+# long dense rows: the kernel's loop rate with few blocks' fixed costs and no
+# masked tiles (informational, not one of the parity configurations)
+MHA_DENSE_LONG = Prefill("MHA dense prefill bf16 B1 H32 S16384 d128", 1, 32, 32, 16384, 16384, 128, False, 0, "bf16", 5)
 INT8_DECODE = Decode("GQA decode over int8 KV cache B32 Hq32 Hkv8 Skv32768 d128", 32, 32, 8, 32768, 128, 4)
 INT4_DECODE = Decode("GQA decode over int4 KV cache B32 Hq32 Hkv8 Skv32768 d128", 32, 32, 8, 32768, 128, 5, bits=4)
 
