@@ -43,8 +43,6 @@ MIN_OCCUPANCY = {
     "decode_split_kernel<128,4,1,1>": 2,
     "decode_merge_kernel<64>": 8,
     "decode_merge_kernel<128>": 8,
-    "bwd_pre_kernel<64>": 8,
-    "bwd_pre_kernel<128>": 8,
     "bwd_dq_kernel<64>": 2,
     "bwd_dq_kernel<128>": 2,
     "bwd_dkdv_kernel<64>": 2,

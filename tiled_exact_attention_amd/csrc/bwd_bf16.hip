@@ -9,16 +9,16 @@
 // the gradients of the forward's definition (D equals rowsum(P * dP) because
 // O = P V).  Nothing of size S x S reaches HBM.
 //
-// Three kernels on the caller's stream:
-//  * bwd_pre_kernel: D and lse * log2(e) per query row into the workspace
-//    (one pass over O and dO; a row with no visible key gets +inf, so its
-//    recomputed probabilities are exactly 0).
+// Two kernels (three for split groups) on the caller's stream:
 //  * bwd_dq_kernel: the forward's layout (4 waves x 32 query rows, GQA head
 //    chunks, K/V tiles of 64 keys streamed HBM -> LDS by LDS-DMA into the
-//    swizzled layout).  Per tile S^T = K Q^T and dP^T = V dO^T (A = K / V rows
-//    from LDS, B = the wave's Q / dO rows held in registers); dS^T lands in
-//    the B-operand layout; dQ^T += K^T dS^T with K^T from transposed LDS
-//    reads.  No running max: lse is known.
+//    swizzled layout).  Each wave first forms D and lse * log2(e) of its rows
+//    (from its dO rows and O) and writes them to the workspace; a row with no
+//    visible key gets +inf, so its recomputed probabilities are exactly 0.
+//    Per tile S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = the
+//    wave's Q / dO rows held in registers); dS^T lands in the B-operand
+//    layout; dQ^T += K^T dS^T with K^T from transposed LDS reads.  No running
+//    max: lse is known.
 //  * bwd_dkdv_kernel: 4 waves x 32 keys, K and V rows in registers as B
 //    operands; query tiles of 64 rows (Q, dO, lse, D) stream through LDS for
 //    every query head of (a split of) the kv head's group and every tile that
@@ -103,33 +103,6 @@ struct BwdParams {
   int causal, window;
 };
 
-// ---------------------------------------------------------------- D and lse2
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int L = D / 8;           // lanes per row, 8 values each
-  constexpr int RPB = 256 / L;       // rows per block
-  const int64_t rows = int64_t(p.B) * p.Sq * p.Hq;  // row = (b, i, h), h fastest
-  const int64_t r = int64_t(blockIdx.x) * RPB + threadIdx.x / L;
-  const int li = threadIdx.x % L;
-  const int64_t rr = r < rows ? r : rows - 1;
-  const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(p.o + rr * D + 8 * li);
-  const bf16x8 d8 = *reinterpret_cast<const bf16x8*>(p.dout + rr * D + 8 * li);
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc = fmaf(float(o8[e]), float(d8[e]), acc);
-#pragma unroll
-  for (int m = 1; m < L; m <<= 1) acc += __shfl_xor(acc, m);
-  if (r >= rows || li != 0) return;
-  const int h = int(r % p.Hq);
-  const int64_t bi = r / p.Hq;
-  const int i = int(bi % p.Sq);
-  const int64_t b = bi / p.Sq;
-  const int64_t idx = (b * p.Hq + h) * p.Sq + i;
-  const float lse = p.lse[idx];
-  p.dd[idx] = acc;
-  p.l2[idx] = lse == -INFINITY ? INFINITY : lse * kLog2e;
-}
-
 // ------------------------------------------------------------------------ dQ
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
@@ -203,9 +176,37 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       df[m] = *reinterpret_cast<const bf16x8*>(p.dout + ro + 16 * m + 8 * hh);
     }
   }
+  // D = rowsum(dO * O) and lse2 = lse * log2(e) (+inf for a row that sees no
+  // key) of this lane's row; the dK/dV kernel reads them from the workspace.
+  // Each 8-value chunk is an fma chain from 0 and the chunk sums are added as a
+  // balanced tree (pairs of neighbouring chunks first); this lane holds chunks
+  // 2m + hh, its partner lane ^ 32 the others.
   const int64_t srow = (int64_t(b) * p.Hq + hq) * Sq + (row_ok ? pos : 0);
-  const float l2 = row_ok ? p.l2[srow] : INFINITY;
-  const float dd = row_ok ? p.dd[srow] : 0.f;
+  float l2, dd;
+  {
+    const int64_t ro = ((int64_t(b) * Sq + (row_ok ? pos : 0)) * p.Hq + hq) * D;
+    float c[KSTEPS];
+#pragma unroll
+    for (int m = 0; m < KSTEPS; ++m) {
+      const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(p.o + ro + 16 * m + 8 * hh);
+      c[m] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[m] = fmaf(float(o8[e]), float(df[m][e]), c[m]);
+      c[m] += __shfl_xor(c[m], 32);  // chunks 2m and 2m + 1
+    }
+#pragma unroll
+    for (int span = 1; span < KSTEPS; span <<= 1) {
+#pragma unroll
+      for (int m = 0; m < KSTEPS; m += 2 * span) c[m] += c[m + span];
+    }
+    const float lse = row_ok ? p.lse[srow] : -INFINITY;
+    l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    dd = row_ok ? c[0] : 0.f;
+    if (hh == 0 && row_ok) {
+      p.dd[srow] = dd;
+      p.l2[srow] = l2;
+    }
+  }
 
   // ---- LDS read offsets (as the forward): row reads of K and V (A operands
   // of S^T and dP^T), transposed reads of K (A operand of dQ^T = K^T dS^T)
@@ -779,13 +780,11 @@ int heads_per_chunk_shift(int G) {
 }
 
 template <int D>
-hipError_t launch_all(const BwdParams& p, int64_t pre_blocks, int64_t dq_blocks, int64_t kv_blocks,
-                      hipStream_t stream) {
-  // each kernel reads what the previous ones wrote: stop at the first
-  // launch that fails, so none runs on a workspace that was never filled
-  hipError_t err = launch_kernel(bwd_pre_kernel<D>, dim3(unsigned(pre_blocks)), dim3(256), 0, stream, p);
-  if (err == hipSuccess)
-    err = launch_kernel(bwd_dq_kernel<D>, dim3(unsigned(dq_blocks)), dim3(kThreads), 0, stream, p);
+hipError_t launch_all(const BwdParams& p, int64_t dq_blocks, int64_t kv_blocks, hipStream_t stream) {
+  // each kernel reads what the previous ones wrote (the dQ kernel fills the
+  // row statistics the dK/dV kernel reads): stop at the first launch that
+  // fails, so none runs on a workspace that was never filled
+  hipError_t err = launch_kernel(bwd_dq_kernel<D>, dim3(unsigned(dq_blocks)), dim3(kThreads), 0, stream, p);
   if (err == hipSuccess)
     err = launch_kernel(bwd_dkdv_kernel<D>, dim3(unsigned(kv_blocks)), dim3(kThreads), 0, stream, p);
   if (err == hipSuccess && p.nsplit > 1) {
@@ -844,15 +843,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   p.part_k = a.part_k;
   p.part_v = a.part_v;
   if (p.nsplit > 1 && (!p.part_k || !p.part_v)) return hipErrorInvalidValue;
-  const int64_t rows = int64_t(a.B) * a.Sq * a.Hq;
-  const int64_t rpb = 256 / (a.d / 8);
-  const int64_t pre_blocks = (rows + rpb - 1) / rpb;
   const int64_t dq_blocks = int64_t(p.nqb) * p.nx;
   const int64_t kv_blocks = int64_t(a.B) * a.Hkv * p.nsplit * ((a.Skv + kBK - 1) / kBK);
-  if (pre_blocks > 0x7fffffff || dq_blocks > 0x7fffffff || kv_blocks > 0x7fffffff)
-    return hipErrorInvalidConfiguration;
-  if (a.d == 64) return launch_all<64>(p, pre_blocks, dq_blocks, kv_blocks, stream);
-  return launch_all<128>(p, pre_blocks, dq_blocks, kv_blocks, stream);
+  if (dq_blocks > 0x7fffffff || kv_blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.d == 64) return launch_all<64>(p, dq_blocks, kv_blocks, stream);
+  return launch_all<128>(p, dq_blocks, kv_blocks, stream);
 }
 
 }  // namespace fattn
