@@ -85,8 +85,8 @@ struct BwdParams {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* l2;   // workspace [B, Hq, Sq]: lse * log2(e), +inf for a row with no key
-  float* dd;   // workspace [B, Hq, Sq]: D = rowsum(dO * O)
+  float* l2;   // workspace [B, Hq, Sq]: lse * log2(e), +inf for a row with no key (written by the dQ kernel)
+  float* dd;   // workspace [B, Hq, Sq]: D = rowsum(dO * O) (written by the dQ kernel)
   float* part_k;  // workspace [nsplit, B, Skv, Hkv, d] fp32 partial dK (nsplit > 1)
   float* part_v;  // ... and dV
   int nsplit;     // query-head splits of a kv head's group in the dK/dV kernel
