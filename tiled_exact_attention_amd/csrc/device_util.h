@@ -202,6 +202,25 @@ __device__ __forceinline__ void store_tile_rows_bf16(char* stage, const f32x16* 
 // returned Sq is the sequence's own length, so the causal diagonal (offset
 // Skv_b - Sq_b) stays right for a sequence longer than that bound, whose
 // rows past the grid are then simply not computed (Skv is unused).
+// Unsigned division by a run-time divisor d (1 <= d < 2^31) of a numerator
+// below 2^31, as a multiply-high, an add and a shift (the round-up method of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, a / d = (mulhi(a, m) + a) >> l.  The
+// multiplier is formed on the host; on uniform values the quotient stays on
+// the scalar unit (a plain division by a kernel argument is expanded through
+// the vector unit's reciprocal, per lane).
+struct UDiv {
+  uint32_t m = 1, l = 0;
+  static UDiv make(uint32_t d) {
+    UDiv r;
+    while ((uint32_t(1) << r.l) < d) ++r.l;
+    r.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << r.l) - d)) / d + 1);
+    return r;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t a) const { return (__umulhi(a, m) + a) >> l; }
+};
+
 struct SeqView {
   int Sq, Skv;
   int64_t q_row0, k_row0;   // first packed row of the sequence

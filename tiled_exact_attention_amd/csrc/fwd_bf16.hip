@@ -98,6 +98,7 @@ struct Params {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  UDiv div_nx, div_nqb, div_nchunk, div_hkv;  // by nx, nqb, nchunk and Hkv
 };
 
 template <int D>
@@ -134,16 +135,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   int x, slot;
   if (p.cu_q && (p.nx & 7) == 0) {
     const int xcd = id & 7, l = id >> 3;
-    slot = l % p.nqb;
-    x = (l / p.nqb) * 8 + xcd;
+    const int pair = int(p.div_nqb.div(uint32_t(l)));
+    slot = l - pair * p.nqb;
+    x = pair * 8 + xcd;
   } else {
-    x = id % p.nx;
-    slot = id / p.nx;
+    slot = int(p.div_nx.div(uint32_t(id)));
+    x = id - slot * p.nx;
   }
   const int qb = p.causal ? p.nqb - 1 - slot : slot;
-  const int chunk = x % p.nchunk;
-  const int hk = (x / p.nchunk) % p.Hkv;
-  const int b = x / (p.nchunk * p.Hkv);
+  const int xc = int(p.div_nchunk.div(uint32_t(x)));  // x / nchunk
+  const int chunk = x - xc * p.nchunk;
+  const int b = int(p.div_hkv.div(uint32_t(xc)));
+  const int hk = xc - b * p.Hkv;
   const int gc = 1 << p.gc_shift;
   const int rows_pos = kBM >> p.gc_shift;     // positions per block
   const int p0 = qb * rows_pos;
@@ -517,6 +520,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.total_k = a.total_k;
   const int64_t blocks = int64_t(p.nqb) * p.nx;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  p.div_nx = UDiv::make(uint32_t(p.nx));
+  p.div_nqb = UDiv::make(uint32_t(p.nqb));
+  p.div_nchunk = UDiv::make(uint32_t(p.nchunk));
+  p.div_hkv = UDiv::make(uint32_t(p.Hkv));
   return launch_kernel(a.d == 64 ? fwd_bf16_kernel<64> : fwd_bf16_kernel<128>,
                        dim3(unsigned(blocks)), dim3(kThreads), 0, stream, p);
 }
