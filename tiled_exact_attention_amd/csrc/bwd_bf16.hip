@@ -97,6 +97,7 @@ struct BwdParams {
   int nchunk;    // G / GC
   int nqb;       // dQ row blocks per (b, kv head, head chunk)
   int nx;        // B * Hkv * nchunk
+  UDiv div_nx, div_nchunk, div_hkv, div_nbh, div_nsplit;  // dividers of the block mappings
   float c;       // |scale| * log2(e), >= 1e-30
   float scale;   // the signed scale
   int negate;    // 1 if scale < 0 (Q, or K, sign flipped on load)
@@ -119,12 +120,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 
   // ---- block -> (batch, kv head, head chunk, query block); heavy blocks first
   const int id = blockIdx.x;
-  const int x = id % p.nx;
-  const int slot = id / p.nx;
+  const int slot = int(p.div_nx.div(uint32_t(id)));
+  const int x = id - slot * p.nx;
   const int qb = p.causal ? p.nqb - 1 - slot : slot;
-  const int chunk = x % p.nchunk;
-  const int hk = (x / p.nchunk) % p.Hkv;
-  const int b = x / (p.nchunk * p.Hkv);
+  const int xc = int(p.div_nchunk.div(uint32_t(x)));
+  const int chunk = x - xc * p.nchunk;
+  const int b = int(p.div_hkv.div(uint32_t(xc)));
+  const int hk = xc - b * p.Hkv;
   const int gc = 1 << p.gc_shift;
   const int rows_pos = kBM >> p.gc_shift;
   const int p0 = qb * rows_pos;
@@ -414,11 +416,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   // with all its key blocks, cut the kernel's HBM reads on the MHA workload
   // from 735 to 309 MB but was 1-2% slower; the kernel is not bound by HBM.)
   const int nbh = p.B * p.Hkv * p.nsplit;
-  const int x = blockIdx.x % nbh;
-  const int kbi = blockIdx.x / nbh;
-  const int split = x % p.nsplit;
-  const int hk = (x / p.nsplit) % p.Hkv;
-  const int b = x / (p.nsplit * p.Hkv);
+  const int kbi = int(p.div_nbh.div(blockIdx.x));
+  const int x = int(blockIdx.x) - kbi * nbh;
+  const int xs = int(p.div_nsplit.div(uint32_t(x)));
+  const int split = x - xs * p.nsplit;
+  const int b = int(p.div_hkv.div(uint32_t(xs)));
+  const int hk = xs - b * p.Hkv;
   const int g0 = split * p.hps;                    // first query head (in the group) of the split
   const int ng = min(p.hps, p.G - g0);             // heads of this split
   const int Sq = p.Sq, Skv = p.Skv;
@@ -492,9 +495,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     ld_row[i] = r;
     goff[i] = uint32_t(r) * uint32_t(q_stride) + ((lane % KCH) ^ swz<D>(r)) * 8;
   }
-  auto issue_loads = [&](int it, char* stage) __attribute__((always_inline)) {
-    const int g = g0 + it / ntq;
-    const int i0 = (tq0 + it % ntq) * kBQ;
+  auto issue_loads = [&](int g, int i0, char* stage) __attribute__((always_inline)) {
     const int hq = hk * p.G + g;
     const __bf16* qb = p.q + (int64_t(b) * Sq * p.Hq + hq) * D;
     const __bf16* db = p.dout + (int64_t(b) * Sq * p.Hq + hq) * D;
@@ -704,11 +705,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     return full ? 2 : 1;
   };
 
+  // (head, query tile) of the tile in the current stage and of the next
+  // load, advanced by counting (iteration it is head g0 + it / ntq, tile
+  // tq0 + it % ntq)
+  int cur_i0 = tq0 * kBQ, ld_g = g0, ld_tq = 0;
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (++ld_tq == ntq) {
+      ld_tq = 0;
+      ++ld_g;
+    }
+  };
   auto step = [&](int it, char* cur, char* nxt) __attribute__((always_inline)) {
     wait_vmcnt<0>();
     __syncthreads();
-    if (it + 1 < niter) issue_loads(it + 1, nxt);
-    const int i0 = (tq0 + it % ntq) * kBQ;
+    const int i0 = cur_i0;
+    if (it + 1 < niter) {
+      advance();
+      cur_i0 = (tq0 + ld_tq) * kBQ;
+      issue_loads(ld_g, cur_i0, nxt);
+    }
     const int cls = tile_class(i0);
     if (cls == 2) {
       compute(i0, cur, std::false_type{});
@@ -716,7 +731,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
       compute(i0, cur, std::true_type{});
     }
   };
-  if (niter > 0) issue_loads(0, lds);
+  if (niter > 0) issue_loads(g0, cur_i0, lds);
   for (int it = 0; it < niter; it += 2) {
     step(it, lds, lds + STAGE_B);
     if (it + 1 < niter) step(it + 1, lds + STAGE_B, lds);
@@ -846,6 +861,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   const int64_t dq_blocks = int64_t(p.nqb) * p.nx;
   const int64_t kv_blocks = int64_t(a.B) * a.Hkv * p.nsplit * ((a.Skv + kBK - 1) / kBK);
   if (dq_blocks > 0x7fffffff || kv_blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  p.div_nx = UDiv::make(uint32_t(p.nx));
+  p.div_nchunk = UDiv::make(uint32_t(p.nchunk));
+  p.div_hkv = UDiv::make(uint32_t(p.Hkv));
+  p.div_nbh = UDiv::make(uint32_t(a.B * a.Hkv * p.nsplit));
+  p.div_nsplit = UDiv::make(uint32_t(p.nsplit));
   if (a.d == 64) return launch_all<64>(p, dq_blocks, kv_blocks, stream);
   return launch_all<128>(p, dq_blocks, kv_blocks, stream);
 }
