@@ -178,6 +178,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     }
   }
   const int ntiles = je > jb ? int((je - jb + kBN - 1) / kBN) : 0;
+  // the lowest row_hi and the highest row_lo among the wave's rows (its first
+  // and last rows; wave-uniform)
+  int w_lo_max = 0, w_hi_min = Skv;
+  if (p.causal) {
+    const int pos_a = p0 + ((w * 32) >> p.gc_shift), pos_b = p0 + ((w * 32 + 31) >> p.gc_shift);
+    w_hi_min = int(min(int64_t(Skv), pos_a + off + 1));
+    if (p.window > 0) w_lo_max = int(max(int64_t(0), pos_b + off - p.window + 1));
+  }
 
   // ---- Q rows of this wave as the B operand (k-step m: columns 16m + 8hh .. +7)
   bf16x8 qf[KSTEPS];
@@ -317,21 +325,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     }
   };
 
-  // ---- S(t) -> P(t): mask (only on tiles that straddle an edge of this
-  // wave's band), online softmax in base 2 with the scale folded into c.
+  // ---- S(t) -> P(t): mask (only on tiles that may straddle an edge of the
+  // block's band), online softmax in base 2 with the scale folded into c.
   auto softmax = [&](int64_t j0, auto masked, auto first) __attribute__((always_inline)) {
     // key j0 + kofs is visible iff row_lo <= key < row_hi; kofs - 4*hh is a
     // compile-time constant per register, so compare against shifted bounds.
+    // The bounds rise with the lane's row, so the wave's first and last rows
+    // bound them all: scalar tests find the 32-key blocks of S that an edge
+    // cuts for some row of the wave, and only those get per-element compares
+    // (one per element and edge).
     if constexpr (decltype(masked)::value) {
       const int jj = int(j0);  // j0 < Skv fits an int
-      const int lo = max(min(row_lo - jj, kBN), -1) - 4 * hh;
-      const int hi = max(min(row_hi - jj, kBN), -1) - 4 * hh;
+      // each test guards a plain if-then that updates s in place (no else
+      // branch), so the results stay in the registers of s
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const int b0 = jj + 32 * kb;  // first key of the block
+        if (w_hi_min < b0 + 32) {     // the causal edge (or the end of the keys) cuts the block for some row
+          const int hi = row_hi - b0 - 4 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kc0 = kb * 32 + 8 * (r >> 2) + (r & 3);
-          if (kc0 < lo || kc0 >= hi) s[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int kc0 = 8 * (r >> 2) + (r & 3);
+            if (kc0 >= hi) s[kb][r] = -INFINITY;
+          }
+        }
+        if (w_lo_max > b0) {  // the window edge cuts the block for some row
+          const int lo = row_lo - b0 - 4 * hh;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kc0 = 8 * (r >> 2) + (r & 3);
+            if (kc0 < lo) s[kb][r] = -INFINITY;
+          }
         }
       }
     }
