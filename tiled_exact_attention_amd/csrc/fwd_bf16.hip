@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   // last tile of the sequence, rows past the end re-read the last row
   auto issue_tile = [&](const __bf16* base, int64_t j0, char* dst_tile) __attribute__((always_inline)) {
     const char* src = reinterpret_cast<const char*>(base + j0 * kv_stride);
-    if (j0 + kBN <= Skv) {
+    if (int(j0) + kBN <= Skv) {  // j0 < Skv < 2^31: a scalar compare
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
         buffer_to_lds16(src, goff[i], dst_tile + (16 * w + LPI * i) * ROWB);
@@ -267,40 +267,45 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   f32x16 s[2];   // S^T of the current tile (two 32-key blocks)
   bf16x8 pf[4];  // P of the previous tile, the B operand of O^T += V^T P^T
 
-  // ---- one block of matrix products: S(t) = K(t) Q^T (if QK) and
-  // O^T += V(t-1)^T P(t-1)^T (if PV).  The products are issued as
-  // interleaved accumulation chains; the LDS operand reads are placed kLA
-  // products ahead of their use (sched_group_barrier: 0x100 = LDS read,
-  // 0x008 = matrix product).
+  // ---- one block of matrix products: S(t) = K(t) Q^T over the first QK
+  // 32-key blocks of the tile, and O^T += V(t-1)^T P(t-1)^T over the first PV
+  // 32-key blocks of the previous tile (QK, PV in 0..2).  The products are
+  // issued as interleaved accumulation chains; the LDS operand reads are
+  // placed kLA products ahead of their use (sched_group_barrier: 0x100 = LDS
+  // read, 0x008 = matrix product).
   auto products = [&](const char* kt, const char* vt, auto QK, auto PV) __attribute__((always_inline)) {
-    constexpr bool qk = decltype(QK)::value, pv = decltype(PV)::value;
-    constexpr int NQK = 2 * KSTEPS, NPV = 4 * NB;  // products; K reads = NQK, V^T reads = 2 * NPV
+    constexpr int qk = decltype(QK)::value, pv = decltype(PV)::value;
+    constexpr int NQK = qk * KSTEPS, NPV = 2 * pv * NB;  // products; K reads = NQK, V^T reads = 2 * NPV
     // A distinct marker per variant keeps the compiler from hoisting the
     // operand reads the variants share above the branch that selects them
     // (which would hold all of them in registers at once).
-    if constexpr (qk && pv) {
+    if constexpr (qk == 2 && pv == 2) {
       asm volatile("; products: S and PV" ::: "memory");
-    } else if constexpr (qk) {
+    } else if constexpr (qk == 1 && pv == 2) {
+      asm volatile("; products: S (first half) and PV" ::: "memory");
+    } else if constexpr (qk == 2) {
       asm volatile("; products: S" ::: "memory");
-    } else {
+    } else if constexpr (pv == 2) {
       asm volatile("; products: PV" ::: "memory");
+    } else {
+      asm volatile("; products: PV (first half)" ::: "memory");
     }
-    if constexpr (qk) {
+    if constexpr (qk > 0) {
       bf16x8 ka[KSTEPS][2];
 #pragma unroll
       for (int m = 0; m < KSTEPS; ++m)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ka[m][kb] = *reinterpret_cast<const bf16x8*>(kt + koff[m] + kb * 32 * ROWB);
-      s[0] = f32x16{};
-      s[1] = f32x16{};
+        for (int kb = 0; kb < qk; ++kb) ka[m][kb] = *reinterpret_cast<const bf16x8*>(kt + koff[m] + kb * 32 * ROWB);
+#pragma unroll
+      for (int kb = 0; kb < qk; ++kb) s[kb] = f32x16{};
 #pragma unroll
       for (int m = 0; m < KSTEPS; ++m)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(ka[m][kb], qf[m], s[kb]);
+        for (int kb = 0; kb < qk; ++kb) s[kb] = mfma32(ka[m][kb], qf[m], s[kb]);
     }
-    if constexpr (pv) {
+    if constexpr (pv > 0) {
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int kc = 0; kc < 2 * pv; ++kc) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const i16x4 a0 = lds_read_tr16(vt + voff[nb][0] + kc * 16 * ROWB);
@@ -309,25 +314,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
         }
       }
     }
-    if constexpr (qk && pv) {
+    if constexpr (qk > 0 && pv > 0) {
       sched_group<0x100, 2 * kLA>();
       sched_pairs<0x008, 1, 0x100, 1, NQK>();
       sched_pairs<0x008, 1, 0x100, 2, NPV - kLA>();
       sched_group<0x008, kLA>();
-    } else if constexpr (qk) {
+    } else if constexpr (qk > 0) {
       sched_group<0x100, 2 * kLA>();
       sched_pairs<0x008, 1, 0x100, 1, NQK - 2 * kLA>();
       sched_group<0x008, 2 * kLA>();
-    } else if constexpr (pv) {
+    } else if constexpr (pv > 0) {
       sched_group<0x100, 2 * kLA>();
       sched_pairs<0x008, 1, 0x100, 2, NPV - kLA>();
       sched_group<0x008, kLA>();
     }
   };
+  using None = std::integral_constant<int, 0>;
+  using Half = std::integral_constant<int, 1>;
+  using Full = std::integral_constant<int, 2>;
 
   // ---- S(t) -> P(t): mask (only on tiles that may straddle an edge of the
   // block's band), online softmax in base 2 with the scale folded into c.
-  auto softmax = [&](int64_t j0, auto masked, auto first) __attribute__((always_inline)) {
+  auto softmax = [&](int64_t j0, auto masked, auto first, auto NKB) __attribute__((always_inline)) {
+    constexpr int nkb = decltype(NKB)::value;  // 32-key blocks of S formed (the rest lie past the band)
     // key j0 + kofs is visible iff row_lo <= key < row_hi; kofs - 4*hh is a
     // compile-time constant per register, so compare against shifted bounds.
     // The bounds rise with the lane's row, so the wave's first and last rows
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
       // each test guards a plain if-then that updates s in place (no else
       // branch), so the results stay in the registers of s
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < nkb; ++kb) {
         const int b0 = jj + 32 * kb;  // first key of the block
         if (w_hi_min < b0 + 32) {     // the causal edge (or the end of the keys) cuts the block for some row
           const int hi = row_hi - b0 - 4 * hh;
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     auto raise_reference = [&]() __attribute__((always_inline)) {
       float mx = kNegHuge;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < nkb; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       }
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     auto exponentials = [&]() __attribute__((always_inline)) {
       float ps = 0.f;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int kc = 0; kc < 2 * nkb; ++kc) {
         float e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -441,13 +450,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
   auto iteration = [&](int t, auto odd, auto masked) __attribute__((always_inline)) {
     constexpr int cur = decltype(odd)::value ? 1 : 0;
     const int64_t j0 = begin(t);
-    products(kbuf[cur], vbuf[cur ^ 1], std::true_type{}, std::true_type{});
+    products(kbuf[cur], vbuf[cur ^ 1], Full{}, Full{});
     copies(t, j0, kbuf[cur ^ 1], vbuf[cur]);
-    softmax(j0, masked, std::false_type{});
+    softmax(j0, masked, std::false_type{}, Full{});
   };
+  // The last tile of the band may hold keys of the band in its first 32 rows
+  // only (a window band of W + 15 keys, say); then S is formed, and turned
+  // into probabilities, for those 32 keys alone, and its P^T product skips
+  // the second half.  The pair loops stop one tile early for it.
+  const bool last_half = ntiles >= 2 && je - jb - int64_t(ntiles - 1) * kBN <= kBN / 2;
+  const int nloop = last_half ? ntiles - 1 : ntiles;  // iterations of the pair loops
   auto pair = [&](int t, auto masked) __attribute__((always_inline)) {
     iteration(t, std::true_type{}, masked);
-    if (t + 1 < ntiles) iteration(t + 1, std::false_type{}, masked);
+    if (t + 1 < nloop) iteration(t + 1, std::false_type{}, masked);
   };
   if (ntiles > 0) {
     int t_lo, t_hi;  // odd, t_lo <= t_hi, t_hi - t_lo even
@@ -464,22 +479,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(Params p) {
     issue_tile(kbase, jb, lds_k0);
     {
       const int64_t j0 = begin(0);
-      products(lds_k0, lds_v0, std::true_type{}, std::false_type{});
+      products(lds_k0, lds_v0, Full{}, None{});
       copies(0, j0, lds_k1, lds_v0);
       if (first_full) {
-        softmax(j0, std::false_type{}, std::true_type{});
+        softmax(j0, std::false_type{}, std::true_type{}, Full{});
       } else {
-        softmax(j0, std::true_type{}, std::true_type{});
+        softmax(j0, std::true_type{}, std::true_type{}, Full{});
       }
     }
     int t = 1;
-    for (; t < t_lo && t < ntiles; t += 2) pair(t, std::true_type{});
+    for (; t < t_lo && t < nloop; t += 2) pair(t, std::true_type{});
     for (; t < t_hi; t += 2) pair(t, std::false_type{});
-    for (; t < ntiles; t += 2) pair(t, std::true_type{});
-    // last product: V(ntiles-1) sits in V buffer (ntiles-1) % 2 (one code
-    // path, so the accumulators leave the loop in the same registers)
+    for (; t < nloop; t += 2) pair(t, std::true_type{});
+    const int tl = ntiles - 1;  // K(tl) sits in K buffer tl % 2; V(tl) goes to V buffer tl % 2
+    if (last_half) {
+      // the last tile (never fully visible: its second half lies past the band)
+      const int64_t j0 = begin(tl);
+      products((tl & 1) ? lds_k1 : lds_k0, (tl & 1) ? lds_v0 : lds_v1, Half{}, Full{});
+      copies(tl, j0, lds_k0, (tl & 1) ? lds_v1 : lds_v0);
+      softmax(j0, std::true_type{}, std::false_type{}, Half{});
+    }
+    // last product: V(tl) sits in V buffer tl % 2
     begin(ntiles);
-    products(lds_k0, ((ntiles - 1) & 1) ? lds_v1 : lds_v0, std::false_type{}, std::true_type{});
+    if (last_half) {
+      products(lds_k0, (tl & 1) ? lds_v1 : lds_v0, None{}, Half{});
+    } else {
+      products(lds_k0, (tl & 1) ? lds_v1 : lds_v0, None{}, Full{});
+    }
   }
 
   // ---- epilogue: normalise, write O (bf16, RNE) and lse (natural log).
