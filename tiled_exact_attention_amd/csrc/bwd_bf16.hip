@@ -149,15 +149,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   int64_t row_lo = 0, row_hi = Skv;
   const int wpos_lo = p0 + ((w * 32) >> p.gc_shift);
   const int wpos_hi = min(p0 + ((w * 32 + 31) >> p.gc_shift), Sq - 1);
-  int64_t w_hi_max = Skv, w_lo_min = 0;
+  // the bounds rise with the row: over the wave's rows row_hi runs from
+  // w_hi_min to w_hi_max and row_lo from w_lo_min to w_lo_max (w_lo_max from
+  // the last row even past Sq, as row_lo is for such rows)
+  const int wpos_end = p0 + ((w * 32 + 31) >> p.gc_shift);
+  int64_t w_hi_max = Skv, w_lo_min = 0, w_hi_min = Skv, w_lo_max = 0;
   if (p.causal) {
     je = min(int64_t(Skv), bpos_hi + off + 1);
     row_hi = min(int64_t(Skv), pos + off + 1);
     w_hi_max = min(int64_t(Skv), wpos_hi + off + 1);
+    w_hi_min = min(int64_t(Skv), wpos_lo + off + 1);
     if (p.window > 0) {
       jb = max(int64_t(0), p0 + off - p.window + 1);
       row_lo = max(int64_t(0), pos + off - p.window + 1);
       w_lo_min = max(int64_t(0), wpos_lo + off - p.window + 1);
+      w_lo_max = max(int64_t(0), wpos_end + off - p.window + 1);
     }
   }
   const bool wave_active = wpos_lo < Sq;
@@ -282,14 +288,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     }
     __builtin_amdgcn_s_setprio(0);
     if constexpr (decltype(masked)::value) {
-      const int lo = int(max(min(row_lo - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
-      const int hi = int(max(min(row_hi - j0, int64_t(kBN)), int64_t(-1))) - 4 * hh;
+      // per 32-key block, only where an edge cuts it for some row of the wave
+      // (scalar tests on the wave's lowest row_hi and highest row_lo), one
+      // compare and select per element and edge, each an in-place if-then
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const int64_t b0 = j0 + 32 * kb;  // first key of the block
+        if (w_hi_min < b0 + 32) {
+          const int hi = int(row_hi - b0) - 4 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kc0 = kb * 32 + 8 * (r >> 2) + (r & 3);
-          if (kc0 < lo || kc0 >= hi) s[kb][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int kc0 = 8 * (r >> 2) + (r & 3);
+            if (kc0 >= hi) s[kb][r] = -INFINITY;
+          }
+        }
+        if (w_lo_max > b0) {
+          const int lo = int(row_lo - b0) - 4 * hh;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kc0 = 8 * (r >> 2) + (r & 3);
+            if (kc0 < lo) s[kb][r] = -INFINITY;
+          }
         }
       }
     }
