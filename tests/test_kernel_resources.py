@@ -43,7 +43,7 @@ MIN_OCCUPANCY = {
     "decode_split_kernel<128,4,1,1>": 2,
     "decode_merge_kernel<64>": 8,
     "decode_merge_kernel<128>": 8,
-    "bwd_dq_kernel<64>": 2,
+    "bwd_dq_kernel<64>": 3,
     "bwd_dq_kernel<128>": 2,
     "bwd_dkdv_kernel<64>": 2,
     "bwd_dkdv_kernel<128>": 1,

@@ -312,14 +312,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
         }
       }
     }
-    // P^T = 2^(s c - lse2) as bf16, in the B layout of K^T dS^T
+    // P^T = 2^(s c - lse2).  This kernel has no product with P: at d = 128 P
+    // stays in s in fp32 and dS below is formed from those values; at d = 64
+    // P is kept packed in bf16 (16 registers instead of 32, which keeps that
+    // kernel at three waves per SIMD) and widened back for dS
     bf16x8 pf[4];
+    if constexpr (D >= 128) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      float e[8];
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -l2));
-      pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c, -l2));
+      }
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], p.c, -l2));
+        pf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+      }
     }
     // dP^T = V dO^T, then dS^T = P^T (dP^T - D)
     __builtin_amdgcn_sched_barrier(0);
@@ -349,11 +360,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       float e[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // element i of pf[kc] widened to fp32 from its packed dword (pf stays
-        // packed: one conversion per pair of probabilities, not per element)
-        const uint32_t pw = __builtin_bit_cast(u32x4, pf[kc])[i / 2];
-        e[i] = __builtin_bit_cast(float, (i & 1) ? (pw & 0xffff0000u) : (pw << 16)) *
-               (dp[kc >> 1][8 * (kc & 1) + i] - dd);
+        float pv;
+        if constexpr (D >= 128) {
+          pv = s[kc >> 1][8 * (kc & 1) + i];
+        } else {
+          // element i of pf[kc] widened to fp32 from its packed dword
+          const uint32_t pw = __builtin_bit_cast(u32x4, pf[kc])[i / 2];
+          pv = __builtin_bit_cast(float, (i & 1) ? (pw & 0xffff0000u) : (pw << 16));
+        }
+        e[i] = pv * (dp[kc >> 1][8 * (kc & 1) + i] - dd);
       }
       dsf[kc] = to_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     }
@@ -564,8 +579,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   // over the dP steps, dS = P (dP - D) over the dV steps, a few elements per
   // step.  Each slice is pinned into its step by empty asm operands (the
   // sched_barrier fences order the machine scheduler, not IR-level code
-  // motion).  dS is formed from the bf16 P of the dV products (as in the dQ
-  // kernel, so dK and dQ see the same dS) and overwrites dP in place.
+  // motion).  dS is formed from the bf16 P of the dV products (so dK and dV
+  // use the same P) and overwrites dP in place.
   auto compute = [&](int i0, const char* stage, auto masked) __attribute__((always_inline)) {
     constexpr int NS = 2 * KSTEPS;       // products of S, and of dP
     constexpr int NT = 4 * NB;           // products of dV, and of dK
